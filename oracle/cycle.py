@@ -1,0 +1,37 @@
+"""One whole draft-verify cycle tail in the oracle, step after step.
+
+Order of a cycle (tamsi.dev "DFlash 2 — 3× plus de tokens…", § "L'idée, sans
+le papier"; latenode.com "DFlash 2: un drafter de 3.43×…", opening section):
+the drafter's convs (one call per drafter layer), the draft LM head with the
+top-16 lists, the pair selector's path, then verification of that path against
+the target's block logits.  "mixed" verification sends the first half of the
+requests to the greedy rule and the second half to rejection sampling.
+"""
+
+import numpy as np
+
+from .conv import conv2tap
+from .head import head_topk
+from .selector import select_path
+from .verify import verify_greedy, verify_sample
+
+
+def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192):
+    L = inp["x"].shape[0]
+    ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
+    vals, idx, _ = head_topk(inp["h"], inp["W"], K=K, chunk=head_chunk)
+    P = T - 1
+    vals = vals.reshape(B, P, K)
+    idx = idx.reshape(B, P, K)
+    rank, tok, score, _ = select_path(vals, idx, inp["F_l"], inp["F_r"])
+    logits = inp["target"]
+    out = np.full((B, T), -1, np.int32)
+    n = np.zeros(B, np.int32)
+    g = {"greedy": B, "sample": 0, "mixed": B // 2}[verify]
+    if g > 0:
+        out[:g], n[:g] = verify_greedy(logits[:g], tok[:g])
+    if g < B:
+        out[g:], n[g:] = verify_sample(logits[g:], tok[g:], inp["temperature"], inp["seed"],
+                                       inp["request_id"][g:], inp["pos0"][g:])
+    return {"y": ys, "top_val": vals, "top_idx": idx, "path_rank": rank,
+            "path_tok": tok, "path_score": score, "out_tok": out, "n_emit": n}

@@ -1,0 +1,163 @@
+"""Lossless verification of a drafted block against the target's block logits.
+
+Source: tamsi.dev "DFlash 2 — 3× plus de tokens…", § "Les chiffres qui
+comptent…" (greedy output is exactly the target's; sampling by rejection
+sampling keeps the target distribution); latenode.com "DFlash 2: un drafter de
+3.43×…", opening section and FAQ (same guarantee), § "El desacuerdo empieza…"
+(acceptance length = tokens completed per verification step); myaiexp.com
+"DFlash 2", § コツ (block size 8 means seven draft tokens).
+
+Block layout (reading): T slots; slot 0 is the last verified token, slots
+1..P = T-1 hold the drafts d[0..P-1].  Target row t (t = 0..T-1) is the
+target's next-token distribution after slot t, so draft d[s-1] at slot s is
+checked against row s-1 and row T-1 supplies the bonus token.
+
+Outputs per request: out_tok[0..n] = accepted drafts then one target token,
+-1 after; n_emit = n + 1 in [1, T].
+"""
+
+import math
+
+import numpy as np
+
+from ._arrays import f64, i64
+from .philox import philox4x64_10
+
+TWO_M53 = 2.0 ** -53
+MASK64 = (1 << 64) - 1
+
+
+def verify_greedy(logits, draft):
+    """Greedy: g[t] = argmax_v logits[t][v] (lowest v on ties); accept the
+    longest prefix with d[s-1] == g[s-1]; then emit g[n]."""
+    L = f64(logits)
+    d = i64(draft)
+    B, T, V = L.shape
+    P = T - 1
+    assert d.shape == (B, P)
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_emit = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        g = np.argmax(L[b], axis=-1)  # first maximum
+        n = 0
+        while n < P and d[b, n] == g[n]:
+            out[b, n] = d[b, n]
+            n += 1
+        out[b, n] = g[n]
+        n_emit[b] = n + 1
+    return out, n_emit
+
+
+def uniforms(seed, request_id, position):
+    """Two 53-bit uniforms in [0, 1) for one decided slot.
+
+    Philox4x64-10 keyed (seed, 0) on counter (1, request_id, position, 0);
+    u_acc comes from output word 0 and u_res from word 1, each as
+    (w >> 11) * 2^-53.  The counter depends on the request's id and the
+    absolute position only, never on the batch slot, so a request's draws do
+    not change with batch composition.
+    """
+    w = philox4x64_10((1, request_id & MASK64, position & MASK64, 0), (seed & MASK64, 0))
+    return (w[0] >> 11) * TWO_M53, (w[1] >> 11) * TWO_M53
+
+
+def row_weights(row, inv_tau):
+    """e(v) = exp((l_v - m) * inv_tau), m = max_v l_v, all in float64."""
+    row = np.asarray(row, dtype=np.float64)
+    return np.exp((row - np.max(row)) * inv_tau)
+
+
+def inverse_cdf(weights, target):
+    """Smallest v with sum_{w <= v} weights[w] > target (ascending v).
+
+    If rounding leaves no such v, the last v with non-zero weight."""
+    c = np.cumsum(weights)
+    hit = np.nonzero(c > target)[0]
+    if hit.size:
+        return int(hit[0])
+    return int(np.nonzero(weights > 0)[0][-1])
+
+
+def decide_slot(e, d, u_acc, u_res):
+    """One draft slot: accept d iff u_acc * Z < e(d); otherwise draw from the
+    residual max(0, p - onehot(d)) (p with d removed), renormalised.
+
+    Returns (accepted, token).  With q = onehot(d) the emitted token has law
+    p: P[d] = p(d), P[v != d] = (1 - p(d)) * p(v) / (1 - p(d)) = p(v).
+    """
+    Z = float(np.sum(e))
+    if u_acc * Z < e[d]:
+        return True, int(d)
+    resid = e.copy()
+    resid[d] = 0.0
+    return False, inverse_cdf(resid, u_res * (Z - e[d]))
+
+
+def decide_bonus(e, u_res):
+    """Bonus token after a fully accepted block: draw from p by inverse CDF."""
+    return inverse_cdf(e, u_res * float(np.sum(e)))
+
+
+def verify_sample(logits, draft, temperature, seed, request_id, pos0,
+                  return_margins=False):
+    """Rejection-sampling verification with a deterministic draft.
+
+    Readings taken (the pages give no algorithm):
+    * p_t = softmax(logits[t] / tau) over the full vocabulary, as
+      e_t(v) / Z_t with e_t(v) = exp((l - max) * (1 / tau)), float64.
+    * The draft token is chosen by the selector, not sampled, so the proposal
+      is q = one-hot(d) (``decide_slot``).
+    * If all P drafts are accepted the bonus token comes from row T-1
+      (``decide_bonus``).
+    * Uniforms come from ``uniforms(seed, request_id, pos0 + s)`` for the slot
+      s being decided (s = T for the bonus).
+    Returns (out_tok, n_emit) and, if asked, per-request margins: the smallest
+    distance, relative to the row's mass, of any decision from its boundary.
+    """
+    L = f64(logits)
+    d = i64(draft)
+    rid = i64(request_id)
+    p0 = i64(pos0)
+    B, T, V = L.shape
+    P = T - 1
+    inv_tau = 1.0 / float(np.float32(temperature))
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_emit = np.zeros(B, dtype=np.int32)
+    margins = np.full(B, np.inf)
+    for b in range(B):
+        n = 0
+        for s in range(1, T + 1):
+            u_acc, u_res = uniforms(int(seed), int(rid[b]), int(p0[b]) + s)
+            if s <= P:
+                e = row_weights(L[b, s - 1], inv_tau)
+                tok = int(d[b, s - 1])
+                if return_margins:
+                    Z = float(np.sum(e))
+                    margins[b] = min(margins[b], abs(u_acc * Z - e[tok]) / Z)
+                    resid = e.copy()
+                    resid[tok] = 0.0
+                    margins[b] = min(margins[b], _edge_margin(resid, u_res * (Z - e[tok])))
+                accepted, tok = decide_slot(e, tok, u_acc, u_res)
+                out[b, n] = tok
+                if accepted:
+                    n += 1
+                    continue
+                break
+            e = row_weights(L[b, T - 1], inv_tau)
+            if return_margins:
+                margins[b] = min(margins[b], _edge_margin(e, u_res * float(np.sum(e))))
+            out[b, n] = decide_bonus(e, u_res)
+        n_emit[b] = n + 1
+    if return_margins:
+        return out, n_emit, margins
+    return out, n_emit
+
+
+def _edge_margin(weights, target):
+    """Distance of an inverse-CDF target from its nearest bin edge, over the mass."""
+    c = np.cumsum(weights)
+    total = c[-1] if c[-1] > 0 else 1.0
+    k = int(np.searchsorted(c, target, side="right"))
+    lo = c[k - 1] if k > 0 else 0.0
+    hi = c[k] if k < c.size else math.inf
+    return min(abs(target - lo), abs(hi - target)) / total

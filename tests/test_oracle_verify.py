@@ -1,0 +1,174 @@
+"""Pins for the oracle's verifiers: greedy against the target's own argmax
+continuation; sampling against the target distribution (exact law on a grid
+of uniforms, chi-square on Philox draws) and its closed-form special cases."""
+
+import numpy as np
+import pytest
+from scipy import stats
+
+from oracle.verify import (decide_bonus, decide_slot, row_weights, uniforms,
+                           verify_greedy, verify_sample)
+
+
+# ---------------------------------------------------------------- greedy
+def test_greedy_emits_target_argmax_continuation():
+    rng = np.random.default_rng(0)
+    B, T, V = 64, 8, 50
+    L = rng.standard_normal((B, T, V))
+    g = np.argmax(L, -1)
+    d = g[:, :T - 1].copy()
+    # corrupt drafts at a random slot (or none) per request
+    cut = rng.integers(0, T, B)
+    for b in range(B):
+        if cut[b] < T - 1:
+            d[b, cut[b]] = (g[b, cut[b]] + 1 + rng.integers(0, V - 1)) % V
+    out, n = verify_greedy(L, d)
+    for b in range(B):
+        assert n[b] == min(cut[b], T - 1) + 1
+        assert list(out[b, :n[b]]) == list(g[b, :n[b]])   # every token = target argmax
+        assert np.all(out[b, n[b]:] == -1)
+        if n[b] - 1 < T - 1:
+            assert d[b, n[b] - 1] != g[b, n[b] - 1]        # stopped at a mismatch
+
+
+def test_greedy_all_match_and_first_mismatch():
+    L = np.zeros((2, 4, 6)); L[:, :, 3] = 1.0
+    out, n = verify_greedy(L, np.array([[3, 3, 3], [2, 3, 3]]))
+    assert list(n) == [4, 1]
+    assert list(out[0]) == [3, 3, 3, 3] and list(out[1]) == [3, -1, -1, -1]
+
+
+def test_greedy_ties_lowest_id():
+    L = np.zeros((1, 2, 5)); L[0, 0, [1, 3]] = 2.0
+    out, n = verify_greedy(L, np.array([[3]]))
+    assert n[0] == 1 and out[0, 0] == 1
+
+
+# ---------------------------------------------------------------- sampling
+def p_of(row, tau=1.0):
+    e = np.exp((row - row.max()) / tau)
+    return e / e.sum()
+
+
+def test_slot_law_on_uniform_grid():
+    """The emitted token's law is p exactly: integrate decide_slot over a
+    midpoint grid of (u_acc, u_res); error bounded by the grid step."""
+    rng = np.random.default_rng(1)
+    row = rng.standard_normal(8) * 1.5
+    e = row_weights(row, 1.0)
+    p = p_of(row)
+    N = 4000
+    grid = (np.arange(N) + 0.5) / N
+    for d in range(8):
+        acc = np.mean([decide_slot(e, d, u, 0.5)[0] for u in grid])
+        assert abs(acc - p[d]) <= 1.0 / N
+        res = np.bincount([decide_slot(e, d, 1.0 - 1e-12, u)[1] for u in grid], minlength=8) / N
+        assert res[d] == 0.0
+        law = (1 - acc) * res
+        law[d] += acc
+        assert np.max(np.abs(law - p)) <= 3.0 / N
+    bonus = np.bincount([decide_bonus(e, u) for u in grid], minlength=8) / N
+    assert np.max(np.abs(bonus - p)) <= 2.0 / N
+
+
+def chi2_pvalue(tokens, p, n):
+    obs = np.bincount(tokens, minlength=p.size).astype(np.float64)
+    exp = n * p
+    keep = exp >= 5
+    o = np.append(obs[keep], obs[~keep].sum())
+    e = np.append(exp[keep], exp[~keep].sum())
+    if e[-1] == 0:
+        o, e = o[:-1], e[:-1]
+    return stats.chisquare(o, e).pvalue
+
+
+def test_chi_square_first_token_follows_target():
+    rng = np.random.default_rng(2)
+    V, N = 32, 1 << 14
+    row0 = rng.standard_normal(V) * 2.0
+    L = np.tile(np.stack([row0, rng.standard_normal(V)])[None], (N, 1, 1))
+    d = np.full((N, 1), int(np.argsort(row0)[-3]))  # a plausible, not top, draft
+    out, n = verify_sample(L, d, 1.0, 11, np.arange(N), np.full(N, 500))
+    first = out[:, 0]
+    assert chi2_pvalue(first, p_of(row0), N) > 1e-3
+
+
+def test_chi_square_second_slot_conditional():
+    rng = np.random.default_rng(3)
+    V, N = 24, 1 << 13
+    row0 = rng.standard_normal(V); row0[5] += 4.0   # d0 = 5 accepted often
+    row1 = rng.standard_normal(V) * 1.5
+    L = np.tile(np.stack([row0, row1, rng.standard_normal(V)])[None], (N, 1, 1))
+    d = np.tile(np.array([[5, int(np.argmin(row1))]]), (N, 1))
+    out, n = verify_sample(L, d, 1.0, 12, np.arange(N), np.zeros(N, np.int64))
+    sel = n >= 2
+    assert abs(sel.mean() - p_of(row0)[5]) < 4 * np.sqrt(p_of(row0)[5] * (1 - p_of(row0)[5]) / N)
+    assert chi2_pvalue(out[sel, 1], p_of(row1), int(sel.sum())) > 1e-3
+
+
+def test_temperature_scales_distribution():
+    rng = np.random.default_rng(4)
+    V, N, tau = 16, 1 << 13, 0.5
+    row0 = rng.standard_normal(V)
+    L = np.tile(np.stack([row0, row0])[None], (N, 1, 1))
+    out, _ = verify_sample(L, np.full((N, 1), 0), tau, 13, np.arange(N), np.zeros(N, np.int64))
+    assert chi2_pvalue(out[:, 0], p_of(row0, tau), N) > 1e-3
+
+
+def test_large_margin_always_accepts_and_negative_never():
+    V, N = 40, 2000
+    L = np.zeros((N, 3, V)); L[:, 0, 7] = 50.0; L[:, 1, 9] = -50.0
+    d = np.tile(np.array([[7, 9]]), (N, 1))
+    out, n = verify_sample(L, d, 1.0, 3, np.arange(N), np.zeros(N, np.int64))
+    assert np.all(out[:, 0] == 7)          # p(7) rounds to 1: always accepted
+    assert np.all(n == 2)                  # slot 2 rejected (prob 2^-53 otherwise)
+    assert np.all(out[:, 1] != 9)          # residual never emits the rejected draft
+
+
+def test_equal_logits_are_uniform():
+    V, N = 20, 1 << 13
+    L = np.zeros((N, 2, V))
+    out, _ = verify_sample(L, np.full((N, 1), 0), 1.0, 21, np.arange(N), np.zeros(N, np.int64))
+    assert chi2_pvalue(out[:, 0], np.full(V, 1.0 / V), N) > 1e-3
+
+
+def test_batch_composition_invariance():
+    rng = np.random.default_rng(5)
+    B, T, V = 12, 5, 30
+    L = rng.standard_normal((B, T, V)) * 3
+    d = rng.integers(0, V, (B, T - 1))
+    rid = rng.integers(0, 2**62, B)
+    pos = rng.integers(0, 2**40, B)
+    out, n = verify_sample(L, d, 1.0, 9, rid, pos)
+    perm = rng.permutation(B)
+    out2, n2 = verify_sample(L[perm], d[perm], 1.0, 9, rid[perm], pos[perm])
+    assert np.array_equal(out2, out[perm]) and np.array_equal(n2, n[perm])
+    sub = perm[:3]
+    out3, n3 = verify_sample(L[sub], d[sub], 1.0, 9, rid[sub], pos[sub])
+    assert np.array_equal(out3, out[sub])
+
+
+def test_philox_visible_through_residual_draw():
+    """All-equal logits over V = 2^k + 1 and d = V - 1: the residual has 2^k
+    equal weights, so the replacement token is exactly floor(u_res * 2^k) =
+    w1 >> (64 - k) whenever slot 1 rejects."""
+    k = 10
+    V = (1 << k) + 1
+    N = 300
+    L = np.zeros((N, 2, V))
+    out, n = verify_sample(L, np.full((N, 1), V - 1), 1.0, 5, np.arange(N), np.full(N, 7))
+    for b in range(N):
+        u_acc, u_res = uniforms(5, b, 8)
+        if u_acc * V >= 1.0:                      # rejected
+            assert out[b, 0] == int(u_res * (1 << k))
+
+
+def test_chi_square_bonus_token_after_full_accept():
+    rng = np.random.default_rng(6)
+    V, N = 28, 1 << 13
+    row0 = np.zeros(V); row0[4] = 60.0              # slot 1 always accepted
+    row1 = rng.standard_normal(V) * 1.5
+    L = np.tile(np.stack([row0, row1])[None], (N, 1, 1))
+    out, n = verify_sample(L, np.full((N, 1), 4), 1.0, 17, np.arange(N), np.zeros(N, np.int64))
+    assert np.all(n == 2) and np.all(out[:, 0] == 4)
+    assert chi2_pvalue(out[:, 1], p_of(row1), N) > 1e-3
