@@ -1,0 +1,290 @@
+#!/usr/bin/env python3
+"""Draft-verify cycles/s of the DFlash 2 cycle tail on one MI355X.
+
+One step = one cycle tail over one batch of synthetic inputs resident in HBM:
+five two-tap conv calls (one per drafter layer), the LM head with top-16, the
+pair selector, and verification (greedy, sampled, or half of each), each a
+C-ABI call on one stream.  Inputs rotate over enough copies to exceed the
+256 MB Infinity Cache, so every step streams its inputs from HBM.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_topk_traffic.json")
+HEAD_SRC = os.path.join(ROOT, "block_draft_verification_amd", "csrc", "head_topk.hip")
+WORKLOAD_TEXT = {
+    "c1_tiny": "batch 1, block 8, hidden 256, vocab 4096, top-16, selector rank 32, greedy",
+    "c2_b1": "batch 1, block 8, hidden 5120, vocab 151936, top-16, selector rank 192, greedy",
+    "c3_b8": "batch 8, block 8, hidden 5120, vocab 151936, top-16, rank 192, rejection sampling tau=1",
+    "c4_b32": "batch 32, block 8, hidden 5120, vocab 151936, top-16, rank 192, half greedy / half sampled",
+    "c5_stress": "batch 32, block 16, hidden 5120, vocab 262144, top-16, rank 192, greedy, context copy",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--config", default="c2_b1", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="bound on the oracle's timed CPU work")
+    ap.add_argument("--max-sets", type=int, default=64)
+    return ap.parse_args()
+
+
+class CycleRunner:
+    """Pre-bound C-ABI calls for every rotating input set."""
+
+    def __init__(self, dfl, torch, cfg, sets, W, F_l, F_r):
+        dev = W.device
+        B, T, P, L = cfg.B, cfg.T, cfg.P, cfg.L
+        self.cfg = cfg
+        self.torch = torch
+        self.y = [torch.empty_like(sets[0]["x"][l]) for l in range(L)]
+        self.tv = torch.empty((cfg.M, 16), dtype=torch.float32, device=dev)
+        self.ti = torch.empty((cfg.M, 16), dtype=torch.int32, device=dev)
+        self.rank = torch.empty((B, P), dtype=torch.int32, device=dev)
+        self.tok = torch.empty((B, P), dtype=torch.int32, device=dev)
+        self.score = torch.empty((B,), dtype=torch.float32, device=dev)
+        self.out = torch.empty((B, T), dtype=torch.int32, device=dev)
+        self.n = torch.empty((B,), dtype=torch.int32, device=dev)
+        g = {"greedy": B, "sample": 0, "mixed": B // 2}[cfg.verify]
+        self.g = g
+        u8 = torch.uint8
+        self.ws_head = torch.empty(dfl.workspace_bytes("head_topk", cfg.M, cfg.D, cfg.V), dtype=u8, device=dev)
+        self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
+        self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
+                                device=dev)
+        tv3, ti3 = self.tv.view(B, P, 16), self.ti.view(B, P, 16)
+        self.calls = []
+        for s in sets:
+            conv = [dfl.bind_conv2tap(s["x"][l], s["taps"][l], self.y[l]) for l in range(L)]
+            head = dfl.bind_head_topk(s["h"], W, self.tv, self.ti, self.ws_head)
+            sel = dfl.bind_select_path(tv3, ti3, F_l, F_r, self.rank, self.tok, self.score)
+            ver = []
+            if g > 0:
+                ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
+            if g < B:
+                ver.append(dfl.bind_verify_sample(s["target_s"], self.tok[g:], cfg.temperature, cfg.seed,
+                                                  s["rid_s"], s["pos_s"], self.out[g:], self.n[g:], self.ws_s))
+            self.calls.append((conv, head, sel, ver))
+
+    def run(self, i, ev=None):
+        conv, head, sel, ver = self.calls[i % len(self.calls)]
+        if ev is not None:
+            ev[0].record()
+        for c in conv:
+            c()
+        if ev is not None:
+            ev[1].record()
+        head()
+        if ev is not None:
+            ev[2].record()
+        sel()
+        if ev is not None:
+            ev[3].record()
+        for v in ver:
+            v()
+        if ev is not None:
+            ev[4].record()
+
+
+def make_sets(torch, cfg, inp, max_sets):
+    B, g = cfg.B, {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
+    base = {
+        "x": inp["x"], "taps": inp["taps"], "h": inp["h"],
+        "target_g": inp["target"][:g].contiguous() if g > 0 else None,
+        "target_s": inp["target"][g:].contiguous() if g < B else None,
+        "rid_s": inp["request_id"][g:].contiguous(), "pos_s": inp["pos0"][g:].contiguous(),
+    }
+    per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    n_sets = max(2, min(max_sets, math.ceil(512e6 / per_set)))
+    sets = [base]
+    for _ in range(n_sets - 1):
+        sets.append({k: (v.clone() if v is not None else None) for k, v in base.items()})
+    return sets, per_set
+
+
+def head_roofline(cfg, head_us):
+    flops = 2.0 * cfg.M * cfg.V * cfg.D
+    bytes_ = cfg.V * cfg.D * 2 + cfg.M * cfg.D * 2 + cfg.M * 16 * 8
+    ai = flops / bytes_
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    t = head_us * 1e-6
+    traffic = stored_traffic(cfg)
+    if ai < ridge:
+        ach = bytes_ / t / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "dflash_head_topk (head_topk_kernel + head_merge_kernel)",
+                "algorithmic_bytes": int(bytes_), "flops": int(flops),
+                "mfma_frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    ach = flops / t / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "kernel": "dflash_head_topk (head_topk_kernel + head_merge_kernel)",
+            "algorithmic_bytes": int(bytes_), "flops": int(flops),
+            "hbm_frac": round(bytes_ / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+
+def head_source_sha():
+    with open(HEAD_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(cfg):
+    """HBM bytes per head launch from committed rocprofv3 --pmc counters, if
+    they were taken on the current head kernel source and this workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(cfg.name)
+    if not entry or entry.get("head_source_sha") != head_source_sha():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
+    """The oracle, as it stands, on the host's cores, on this run's inputs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle.cycle import run_cycle
+
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    t0 = time.perf_counter()
+    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
+    t1 = time.perf_counter() - t0
+    n, total = 1, t1
+    while total + t1 <= seconds and n < 5:
+        t0 = time.perf_counter()
+        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
+        total += time.perf_counter() - t0
+        n += 1
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    parity = {
+        "conv_bits": all(torch.equal(gpu_res["y"][l].view(torch.int16), ref["y"][l].view(torch.int16))
+                         for l in range(cfg.L)),
+        "top_idx": bool(np.array_equal(gpu_res["ti"], ref["top_idx"].reshape(-1, 16))),
+        "path_tok": bool(np.array_equal(gpu_res["tok"], ref["path_tok"])),
+        "out_tok": bool(np.array_equal(gpu_res["out"], ref["out_tok"])),
+        "n_emit": bool(np.array_equal(gpu_res["n"], ref["n_emit"])),
+    }
+    return {"value": round(n / total, 4), "unit": "cycles/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full {cfg.name} cycle(s) of the float64 numpy oracle on the inputs of "
+                      f"set 0 ({total:.1f} s)",
+            "host_cpus": len(os.sched_getaffinity(0))}, parity
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_draft_verification_amd as dfl
+    from workload import get_config, make_cycle_inputs
+
+    dfl.lib()
+    dev = torch.device("cuda:0")
+    cfg = get_config(args.config)
+    log(f"[bench] config {cfg.name}: generating inputs on {dev}")
+    inp = make_cycle_inputs(cfg, device=dev)
+    sets, per_set = make_sets(torch, cfg, inp, args.max_sets)
+    log(f"[bench] {len(sets)} rotating input sets of {per_set / 1e6:.1f} MB")
+    runner = CycleRunner(dfl, torch, cfg, sets, inp["W"], inp["F_l"], inp["F_r"])
+
+    # warmup (untimed)
+    for i in range(args.warmup):
+        runner.run(i)
+    torch.cuda.synchronize()
+
+    # per-stage events on the stream the kernels run on
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        runner.run(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs]) * 1e3  # us
+    cycle_us = np.array([e[0].elapsed_time(e[4]) for e in evs]) * 1e3
+    head_us = float(stage[:, 1].mean())
+    log(f"[bench] {args.steps} cycles in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
+        f"{ms_per_step * 1e3:.1f} us/cycle; head {head_us:.1f} us")
+
+    # outputs of the last cycle on set 0, for the parity check
+    runner.run(0)
+    torch.cuda.synchronize()
+    gpu_res = {"y": [y.cpu() for y in runner.y], "ti": runner.ti.cpu().numpy(),
+               "tok": runner.tok.cpu().numpy(), "out": runner.out.cpu().numpy(), "n": runner.n.cpu().numpy()}
+
+    rec = {
+        "metric": "draft-verify cycles/sec at block 8, batch 1/8/32; % of HBM/MFMA roofline",
+        "value": round(1e3 / ms_per_step, 2),
+        "unit": "cycles/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT[cfg.name]}", "batch": cfg.B, "block": cfg.T,
+                   "hidden": cfg.D, "vocab": cfg.V, "top_k": 16, "selector_rank": cfg.r,
+                   "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets)},
+        "roofline": head_roofline(cfg, head_us),
+        "stages_us": {"conv_x5": round(float(np.median(stage[:, 0])), 2),
+                      "head_topk": round(float(np.median(stage[:, 1])), 2),
+                      "select_path": round(float(np.median(stage[:, 2])), 2),
+                      "verify": round(float(np.median(stage[:, 3])), 2)},
+        "cycle_us_p10_p50_p90": [round(float(np.percentile(cycle_us, q)), 2) for q in (10, 50, 90)],
+        "mean_n_emit": round(float(gpu_res["n"].mean()), 3),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the same inputs")
+        cb, parity = cpu_baseline(torch, cfg, inp, gpu_res, args.cpu_seconds)
+        rec["cpu_baseline"] = cb
+        rec["parity_vs_oracle"] = parity
+        log(f"[bench] oracle {cb['value']} cycles/s on {cb['cores']} threads; parity {parity}")
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""Python binding of libdflash.so: the DFlash 2 cycle tail on MI355X (gfx950).
+
+Argument marshalling only.  Every step runs in the library's HIP kernels on the
+caller's current torch stream; tensors provide device memory.  There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+
+Entry points (same names and semantics as include/dflash.h):
+    conv2tap(x, taps)                         -> y
+    head_topk(h, W, K=16)                     -> (top_val, top_idx)
+    select_path(top_val, top_idx, F_l, F_r)   -> (path_rank, path_tok, path_score)
+    verify_greedy(logits, draft)              -> (out_tok, n_emit)
+    verify_sample(logits, draft, temperature, seed, request_id, pos0)
+                                              -> (out_tok, n_emit)
+"""
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+_c_i32, _c_i64, _c_u64, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+_p, _psz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+
+_SIGNATURES = {
+    "dflash_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "dflash_version": (ctypes.c_int, []),
+    "dflash_conv2tap": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
+    "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
+    "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                          _p, _p, _p, _p]),
+    "dflash_verify_greedy": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _p, _p, _p, _psz, _p]),
+    "dflash_verify_sample": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p, _p,
+                                            _p, _p, _p, _psz, _p]),
+}
+EXPORTS = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class DFlashError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load libdflash.so once (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DFlashError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code):
+    return lib().dflash_status_string(code).decode()
+
+
+def _check(code, what):
+    if code != 0:
+        raise DFlashError(f"{what}: {status_string(code)} ({code})")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name, dims=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise DFlashError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype != dtype:
+        raise DFlashError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise DFlashError(f"{name} must be contiguous")
+    if dims is not None and t.dim() != dims:
+        raise DFlashError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _workspace(fn, args_before, args_after, device, workspace):
+    """Query the workspace size with a NULL workspace, then allocate if needed."""
+    need = ctypes.c_size_t(0)
+    _check(fn(*args_before, None, ctypes.byref(need), *args_after), fn.__name__ + " (workspace query)")
+    n = max(int(need.value), 16)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    return workspace, ctypes.c_size_t(workspace.numel())
+
+
+def conv2tap(x, taps, out=None):
+    """x bf16 [S][T][D], taps bf16 [S][T][2D] -> y bf16 [S][T][D]."""
+    _need(x, torch.bfloat16, "x")
+    _need(taps, torch.bfloat16, "taps")
+    D = x.shape[-1]
+    T = x.shape[-2]
+    S = x.numel() // (T * D)
+    if taps.shape[-1] != 2 * D or taps.numel() != 2 * x.numel():
+        raise DFlashError("taps must be [..., T, 2*D] matching x")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, torch.bfloat16, "out")
+    _check(lib().dflash_conv2tap(_ptr(x), _ptr(taps), _ptr(y), S, T, D, _stream(x.device)),
+           "dflash_conv2tap")
+    return y
+
+
+def head_topk(h, W, K=16, workspace=None, out=None):
+    """h bf16 [M][D], W bf16 [V][D] -> (top_val f32 [M][K], top_idx i32 [M][K])."""
+    _need(h, torch.bfloat16, "h", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    M, D = h.shape
+    V = W.shape[0]
+    if W.shape[1] != D:
+        raise DFlashError("W must be [V][D] with the same D as h")
+    if out is None:
+        tv = torch.empty((M, K), dtype=torch.float32, device=h.device)
+        ti = torch.empty((M, K), dtype=torch.int32, device=h.device)
+    else:
+        tv, ti = out
+    L = lib()
+    before = (_ptr(h), _ptr(W), M, D, V, K, _ptr(tv), _ptr(ti))
+    ws, nbytes = _workspace(L.dflash_head_topk, before, (_stream(h.device),), h.device, workspace)
+    _check(L.dflash_head_topk(*before, _ptr(ws), ctypes.byref(nbytes), _stream(h.device)),
+           "dflash_head_topk")
+    return tv, ti
+
+
+def select_path(top_val, top_idx, F_l, F_r, out=None):
+    """top_val f32 [B][P][16], top_idx i32 [B][P][16], F_l/F_r f32 [V][r]
+    -> (path_rank i32 [B][P], path_tok i32 [B][P], path_score f32 [B])."""
+    _need(top_val, torch.float32, "top_val", 3)
+    _need(top_idx, torch.int32, "top_idx", 3)
+    _need(F_l, torch.float32, "F_l", 2)
+    _need(F_r, torch.float32, "F_r", 2)
+    B, P, K = top_val.shape
+    V, r = F_l.shape
+    if tuple(F_r.shape) != (V, r) or tuple(top_idx.shape) != (B, P, K):
+        raise DFlashError("shape mismatch in select_path")
+    if out is None:
+        rank = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
+        tok = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
+        score = torch.empty((B,), dtype=torch.float32, device=top_val.device)
+    else:
+        rank, tok, score = out
+    _check(lib().dflash_select_path(_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r,
+                                    _ptr(rank), _ptr(tok), _ptr(score), _stream(top_val.device)),
+           "dflash_select_path")
+    return rank, tok, score
+
+
+def verify_greedy(logits, draft, workspace=None, out=None):
+    """logits f32 [B][T][V], draft i32 [B][T-1] -> (out_tok i32 [B][T], n_emit i32 [B])."""
+    _need(logits, torch.float32, "logits", 3)
+    _need(draft, torch.int32, "draft", 2)
+    B, T, V = logits.shape
+    if tuple(draft.shape) != (B, T - 1):
+        raise DFlashError("draft must be [B][T-1]")
+    if out is None:
+        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
+        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    else:
+        o, n = out
+    L = lib()
+    before = (_ptr(logits), _ptr(draft), B, T, V, _ptr(o), _ptr(n))
+    ws, nbytes = _workspace(L.dflash_verify_greedy, before, (_stream(logits.device),), logits.device,
+                            workspace)
+    _check(L.dflash_verify_greedy(*before, _ptr(ws), ctypes.byref(nbytes), _stream(logits.device)),
+           "dflash_verify_greedy")
+    return o, n
+
+
+def verify_sample(logits, draft, temperature, seed, request_id, pos0, workspace=None, out=None):
+    """Rejection-sampling verification; request_id/pos0 int64 [B] (request ids
+    are taken as their uint64 bit pattern)."""
+    _need(logits, torch.float32, "logits", 3)
+    _need(draft, torch.int32, "draft", 2)
+    _need(request_id, torch.int64, "request_id", 1)
+    _need(pos0, torch.int64, "pos0", 1)
+    B, T, V = logits.shape
+    if tuple(draft.shape) != (B, T - 1) or request_id.numel() != B or pos0.numel() != B:
+        raise DFlashError("shape mismatch in verify_sample")
+    if out is None:
+        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
+        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    else:
+        o, n = out
+    L = lib()
+    before = (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(seed) & (2**64 - 1),
+              _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
+    ws, nbytes = _workspace(L.dflash_verify_sample, before, (_stream(logits.device),), logits.device,
+                            workspace)
+    _check(L.dflash_verify_sample(*before, _ptr(ws), ctypes.byref(nbytes), _stream(logits.device)),
+           "dflash_verify_sample")
+    return o, n
+
+
+# --------------------------------------------------------------------------
+# Pre-marshalled calls for tight loops: each bind_* checks its tensors once and
+# returns a zero-argument callable that makes exactly one C-ABI call on the
+# stream that was current when it was bound (bind inside a graph-capture
+# context to record into the graph).
+
+def _bound(fn, args, what):
+    def call():
+        code = fn(*args)
+        if code != 0:
+            raise DFlashError(f"{what}: {status_string(code)} ({code})")
+    return call
+
+
+def bind_conv2tap(x, taps, y):
+    _need(x, torch.bfloat16, "x")
+    _need(taps, torch.bfloat16, "taps")
+    _need(y, torch.bfloat16, "y")
+    D, T = x.shape[-1], x.shape[-2]
+    S = x.numel() // (T * D)
+    return _bound(lib().dflash_conv2tap, (_ptr(x), _ptr(taps), _ptr(y), S, T, D, _stream(x.device)),
+                  "dflash_conv2tap")
+
+
+def bind_head_topk(h, W, top_val, top_idx, workspace):
+    _need(h, torch.bfloat16, "h", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    M, D = h.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_head_topk,
+                  (_ptr(h), _ptr(W), M, D, W.shape[0], top_val.shape[-1], _ptr(top_val), _ptr(top_idx),
+                   _ptr(workspace), ctypes.byref(nbytes), _stream(h.device)), "dflash_head_topk")
+
+
+def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score):
+    B, P, K = top_val.shape
+    V, r = F_l.shape
+    return _bound(lib().dflash_select_path,
+                  (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
+                   _ptr(score), _stream(top_val.device)), "dflash_select_path")
+
+
+def bind_verify_greedy(logits, draft, out_tok, n_emit, workspace):
+    B, T, V = logits.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_verify_greedy,
+                  (_ptr(logits), _ptr(draft), B, T, V, _ptr(out_tok), _ptr(n_emit), _ptr(workspace),
+                   ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_greedy")
+
+
+def bind_verify_sample(logits, draft, temperature, seed, request_id, pos0, out_tok, n_emit, workspace):
+    B, T, V = logits.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_verify_sample,
+                  (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(seed) & (2**64 - 1),
+                   _ptr(request_id), _ptr(pos0), _ptr(out_tok), _ptr(n_emit), _ptr(workspace),
+                   ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_sample")
+
+
+def workspace_bytes(op, *shape_args):
+    """Workspace size of an entry point for the given sizes, without a GPU call:
+    op in {"head_topk": (M, D, V), "verify_greedy": (B, T, V), "verify_sample": (B, T, V)}."""
+    L = lib()
+    n = ctypes.c_size_t(0)
+    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
+    if op == "head_topk":
+        M, D, V = shape_args
+        code = L.dflash_head_topk(fake[0], fake[1], M, D, V, 16, fake[2], fake[3], None, ctypes.byref(n), None)
+    elif op == "verify_greedy":
+        B, T, V = shape_args
+        code = L.dflash_verify_greedy(fake[0], fake[1], B, T, V, fake[2], fake[3], None, ctypes.byref(n), None)
+    elif op == "verify_sample":
+        B, T, V = shape_args
+        code = L.dflash_verify_sample(fake[0], fake[1], B, T, V, 1.0, 0, fake[4], fake[5], fake[2], fake[3],
+                                      None, ctypes.byref(n), None)
+    else:
+        raise ValueError(op)
+    _check(code, f"workspace query {op}")
+    return max(int(n.value), 16)

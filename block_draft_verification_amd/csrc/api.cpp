@@ -1,0 +1,214 @@
+// C ABI of the cycle-tail library: host-side validation, workspace sizing and
+// dispatch to the gfx950 kernels.  No HIP call happens before an argument check
+// has passed, so every error path can be exercised without a GPU.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/dflash.h"
+
+namespace dflash {
+int launch_conv2tap(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int, hipStream_t);
+int launch_head_topk(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*, void*,
+                     hipStream_t);
+size_t head_workspace_bytes(int64_t M, int64_t V);
+int launch_select_path(const float*, const int32_t*, const float*, const float*, int, int, int64_t, int,
+                       int32_t*, int32_t*, float*, hipStream_t);
+size_t greedy_workspace_bytes(int B, int T, int64_t V);
+size_t sample_workspace_bytes(int B, int T, int64_t V);
+int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
+                         hipStream_t);
+int launch_verify_sample(const float*, const int32_t*, int, int, int64_t, float, uint64_t, const uint64_t*,
+                         const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
+}  // namespace dflash
+
+using namespace dflash;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+
+// Current device must be a gfx950 (MI355X / MI350X).  Cached per device.
+int check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DFLASH_ERR_DEVICE;
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        g_dev_ok[dev] = (hipGetDeviceProperties(&prop, dev) == hipSuccess &&
+                         strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+                            ? 1
+                            : 0;
+    });
+    return g_dev_ok[dev] ? DFLASH_OK : DFLASH_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges)
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int workspace_check(void* ws, size_t* ws_bytes, size_t need, bool* query) {
+    if (!ws_bytes) return DFLASH_ERR_INVALID;
+    if (!ws) {
+        *ws_bytes = need;
+        *query = true;
+        return DFLASH_OK;
+    }
+    *query = false;
+    if (*ws_bytes < need) return DFLASH_ERR_WORKSPACE;
+    if (!aligned16(ws)) return DFLASH_ERR_INVALID;
+    return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(int status) {
+    switch (status) {
+        case DFLASH_OK: return "ok";
+        case DFLASH_ERR_INVALID: return "invalid argument";
+        case DFLASH_ERR_UNSUPPORTED: return "unsupported size";
+        case DFLASH_ERR_WORKSPACE: return "workspace too small";
+        case DFLASH_ERR_LAUNCH: return "kernel launch failed";
+        case DFLASH_ERR_DEVICE: return "current device is not gfx950";
+        default: return "unknown status";
+    }
+}
+
+int dflash_version(void) { return (1 << 16) | 0; }
+
+int dflash_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y, int64_t n_seq, int32_t T,
+                    int32_t D, void* stream) {
+    if (!x || !taps || !y) return DFLASH_ERR_INVALID;
+    if (n_seq < 1 || T < 1 || T > 16 || D < 8 || D % 8 != 0) return DFLASH_ERR_INVALID;
+    if (n_seq > ((int64_t)1 << 40) / ((int64_t)T * D)) return DFLASH_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(taps) || !aligned16(y)) return DFLASH_ERR_INVALID;
+    const size_t nx = (size_t)n_seq * T * D * 2;
+    if (overlap(y, nx, x, nx) || overlap(y, nx, taps, 2 * nx)) return DFLASH_ERR_INVALID;
+    int st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_conv2tap(x, taps, y, n_seq, T, D, (hipStream_t)stream);
+}
+
+int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,
+                     float* top_val, int32_t* top_idx, void* workspace, size_t* workspace_bytes,
+                     void* stream) {
+    if (!h || !W || !top_val || !top_idx) return DFLASH_ERR_INVALID;
+    if (M < 1 || D < 8 || D % 8 != 0 || V < 1) return DFLASH_ERR_INVALID;
+    if (K != 16) return DFLASH_ERR_UNSUPPORTED;
+    if (V < K || V >= ((int64_t)1 << 31) || M > ((int64_t)1 << 24)) return DFLASH_ERR_INVALID;
+    if (!aligned16(h) || !aligned16(W) || !aligned4(top_val) || !aligned4(top_idx)) return DFLASH_ERR_INVALID;
+    const size_t nout = (size_t)M * K * 4;
+    if (overlap(top_val, nout, top_idx, nout) || overlap(top_val, nout, h, (size_t)M * D * 2) ||
+        overlap(top_idx, nout, h, (size_t)M * D * 2) || overlap(top_val, nout, W, (size_t)V * D * 2) ||
+        overlap(top_idx, nout, W, (size_t)V * D * 2))
+        return DFLASH_ERR_INVALID;
+    bool query = false;
+    int st = workspace_check(workspace, workspace_bytes, head_workspace_bytes(M, V), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    if (overlap(workspace, nws, h, (size_t)M * D * 2) || overlap(workspace, nws, W, (size_t)V * D * 2) ||
+        overlap(workspace, nws, top_val, nout) || overlap(workspace, nws, top_idx, nout))
+        return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_head_topk(h, W, M, D, V, top_val, top_idx, workspace, (hipStream_t)stream);
+}
+
+int dflash_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
+                       const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
+                       int32_t* path_rank, int32_t* path_tok, float* path_score, void* stream) {
+    if (!top_val || !top_idx || !feat_l || !feat_r || !path_rank || !path_tok || !path_score)
+        return DFLASH_ERR_INVALID;
+    if (B < 1 || P < 1 || P > 15 || V < 1 || r < 4 || r > 256 || r % 4 != 0) return DFLASH_ERR_INVALID;
+    if (K != 16) return DFLASH_ERR_UNSUPPORTED;
+    if (!aligned4(top_val) || !aligned4(top_idx) || !aligned4(feat_l) || !aligned4(feat_r) ||
+        !aligned4(path_rank) || !aligned4(path_tok) || !aligned4(path_score))
+        return DFLASH_ERR_INVALID;
+    const size_t nbp = (size_t)B * P * 4, nin = (size_t)B * P * K * 4;
+    const void* outs[3] = {path_rank, path_tok, path_score};
+    const size_t outn[3] = {nbp, nbp, (size_t)B * 4};
+    const void* ins[4] = {top_val, top_idx, feat_l, feat_r};
+    const size_t inn[4] = {nin, nin, (size_t)V * r * 4, (size_t)V * r * 4};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 4; ++j)
+            if (overlap(outs[i], outn[i], ins[j], inn[j])) return DFLASH_ERR_INVALID;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], outn[i], outs[j], outn[j])) return DFLASH_ERR_INVALID;
+    }
+    int st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_select_path(top_val, top_idx, feat_l, feat_r, B, P, V, r, path_rank, path_tok, path_score,
+                              (hipStream_t)stream);
+}
+
+static int verify_common_checks(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
+                                int32_t* out_tok, int32_t* n_emit) {
+    if (!logits || !draft || !out_tok || !n_emit) return DFLASH_ERR_INVALID;
+    if (B < 1 || T < 2 || T > 16 || V < 1 || V >= ((int64_t)1 << 31)) return DFLASH_ERR_INVALID;
+    if (!aligned4(logits) || !aligned4(draft) || !aligned4(out_tok) || !aligned4(n_emit))
+        return DFLASH_ERR_INVALID;
+    const size_t nl = (size_t)B * T * V * 4, nd = (size_t)B * (T - 1) * 4, no = (size_t)B * T * 4,
+                 nn = (size_t)B * 4;
+    if (overlap(out_tok, no, logits, nl) || overlap(out_tok, no, draft, nd) || overlap(n_emit, nn, logits, nl) ||
+        overlap(n_emit, nn, draft, nd) || overlap(out_tok, no, n_emit, nn))
+        return DFLASH_ERR_INVALID;
+    return DFLASH_OK;
+}
+
+int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
+                         int32_t* out_tok, int32_t* n_emit, void* workspace, size_t* workspace_bytes,
+                         void* stream) {
+    int st = verify_common_checks(logits, draft, B, T, V, out_tok, n_emit);
+    if (st != DFLASH_OK) return st;
+    bool query = false;
+    st = workspace_check(workspace, workspace_bytes, greedy_workspace_bytes(B, T, V), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    if (overlap(workspace, nws, logits, (size_t)B * T * V * 4) ||
+        overlap(workspace, nws, draft, (size_t)B * (T - 1) * 4) ||
+        overlap(workspace, nws, out_tok, (size_t)B * T * 4) || overlap(workspace, nws, n_emit, (size_t)B * 4))
+        return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_verify_greedy(logits, draft, B, T, V, out_tok, n_emit, workspace, (hipStream_t)stream);
+}
+
+int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
+                         float temperature, uint64_t seed, const uint64_t* request_id, const int64_t* pos0,
+                         int32_t* out_tok, int32_t* n_emit, void* workspace, size_t* workspace_bytes,
+                         void* stream) {
+    int st = verify_common_checks(logits, draft, B, T, V, out_tok, n_emit);
+    if (st != DFLASH_OK) return st;
+    if (!request_id || !pos0 || !(temperature > 0.0f) || !isfinite(temperature)) return DFLASH_ERR_INVALID;
+    if (((uintptr_t)request_id & 7u) || ((uintptr_t)pos0 & 7u)) return DFLASH_ERR_INVALID;
+    const size_t no = (size_t)B * T * 4, nn = (size_t)B * 4, n8 = (size_t)B * 8;
+    if (overlap(out_tok, no, request_id, n8) || overlap(out_tok, no, pos0, n8) ||
+        overlap(n_emit, nn, request_id, n8) || overlap(n_emit, nn, pos0, n8))
+        return DFLASH_ERR_INVALID;
+    bool query = false;
+    st = workspace_check(workspace, workspace_bytes, sample_workspace_bytes(B, T, V), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    if (overlap(workspace, nws, logits, (size_t)B * T * V * 4) ||
+        overlap(workspace, nws, draft, (size_t)B * (T - 1) * 4) || overlap(workspace, nws, out_tok, no) ||
+        overlap(workspace, nws, n_emit, nn) || overlap(workspace, nws, request_id, n8) ||
+        overlap(workspace, nws, pos0, n8))
+        return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_verify_sample(logits, draft, B, T, V, temperature, seed, request_id, pos0, out_tok, n_emit,
+                                workspace, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,476 @@
+// Greedy and rejection-sampling verification of a drafted block (gfx950).
+//
+// Source: tamsi.dev "DFlash 2 - 3x plus de tokens...", section "Les chiffres
+// qui comptent..." (greedy output equals the target's; rejection sampling
+// keeps the target distribution); latenode.com "DFlash 2: un drafter de
+// 3.43x...", FAQ (same guarantee) and section "El desacuerdo empieza..."
+// (acceptance length = tokens completed per verify step).
+//
+// Both verifiers stream the B*T target rows once, split along the vocabulary
+// into 4096-float chunks (one 256-thread workgroup each, 16 floats per thread,
+// 16-byte loads when rows are 16-byte aligned), and write one small record per
+// (row, chunk).  A second kernel, one workgroup per request, takes the
+// per-slot decisions from those records; the sampler re-reads at most the
+// logits of the chunks it inverts the CDF in, plus one logit per slot.
+//
+// Sampling arithmetic is float64 throughout (weights, sums, decisions) so the
+// decisions agree with an exact evaluation except within ~1e-15 of a boundary.
+
+#include "common.hpp"
+
+namespace dflash {
+
+constexpr int kChunk = 4096;
+constexpr int kVerifyThreads = 256;
+constexpr int kPerThread = kChunk / kVerifyThreads;  // 16
+
+struct ChunkStat {  // one per (row, chunk) for the sampler
+    double mass;    // sum over the chunk of exp((l - m_chunk) * inv_tau)
+    float m;        // chunk maximum
+    int pad;
+};
+
+// ----------------------------------------------------------------- reductions
+__device__ __forceinline__ void argmax_combine(float& v, int& i, float v2, int i2) {
+    if (ranks_before(v2, i2, v, i)) {
+        v = v2;
+        i = i2;
+    }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float v2 = __shfl_xor(v, off);
+        const int i2 = __shfl_xor(i, off);
+        argmax_combine(v, i, v2, i2);
+    }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+
+// Block (256 threads) reductions; `scratch` must hold 4 entries; every thread
+// gets the result.
+__device__ float block_max(float v, float* scratch) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) scratch[w] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
+}
+
+__device__ double block_sum(double v, double* scratch) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) scratch[w] = v;
+    __syncthreads();
+    return (scratch[0] + scratch[1]) + (scratch[2] + scratch[3]);
+}
+
+__device__ int block_min_int(int v, int* scratch) {
+    v = wave_min_int(v);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    __syncthreads();
+    if (l == 0) scratch[w] = v;
+    __syncthreads();
+    return min(min(scratch[0], scratch[1]), min(scratch[2], scratch[3]));
+}
+
+// Exclusive prefix sum over the block in thread order; returns the prefix and
+// writes the block total.
+__device__ double block_exclusive_scan(double v, double* scratch, double& total) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    double incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double up = __shfl_up(incl, off);
+        if (l >= off) incl += up;
+    }
+    __syncthreads();
+    if (l == 63) scratch[w] = incl;
+    __syncthreads();
+    double before = 0.0;
+    for (int k = 0; k < w; ++k) before += scratch[k];
+    total = ((scratch[0] + scratch[1]) + scratch[2]) + scratch[3];
+    return before + incl - v;
+}
+
+// ------------------------------------------------------- streaming loaders
+// Loads this thread's (up to) 16 logits of chunk `chunk` of a row.  With VEC
+// the row start is 16-byte aligned and V % 4 == 0: thread t reads float4s at
+// element offsets 4*(t + 256*i), i = 0..3 (coalesced).  Missing elements get
+// -inf and index INT_MAX.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ row, int64_t V, int chunk,
+                                           float (&v)[kPerThread], int (&idx)[kPerThread]) {
+    const int64_t c0 = (int64_t)chunk * kChunk;
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t e = c0 + 4 * ((int64_t)threadIdx.x + kVerifyThreads * i);
+            if (e < V) {
+                const floatx4 q = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(row + e));
+                v[4 * i + 0] = q.x;
+                v[4 * i + 1] = q.y;
+                v[4 * i + 2] = q.z;
+                v[4 * i + 3] = q.w;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) idx[4 * i + j] = (int)(e + j);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v[4 * i + j] = -INFINITY;
+                    idx[4 * i + j] = 0x7FFFFFFF;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) {
+            const int64_t e = c0 + threadIdx.x + (int64_t)kVerifyThreads * i;
+            if (e < V) {
+                v[i] = __builtin_nontemporal_load(row + e);
+                idx[i] = (int)e;
+            } else {
+                v[i] = -INFINITY;
+                idx[i] = 0x7FFFFFFF;
+            }
+        }
+    }
+}
+
+// ================================================================== greedy
+template <bool VEC>
+__global__ __launch_bounds__(kVerifyThreads) void greedy_partial_kernel(
+    const float* __restrict__ logits, int64_t V, int n_chunks, float2* __restrict__ part) {
+    __shared__ float sv[4];
+    __shared__ int si[4];
+    const int64_t row = blockIdx.y;
+    const int chunk = blockIdx.x;
+    float v[kPerThread];
+    int idx[kPerThread];
+    load_chunk<VEC>(logits + row * V, V, chunk, v, idx);
+    float bv = v[0];
+    int bi = idx[0];
+#pragma unroll
+    for (int i = 1; i < kPerThread; ++i) argmax_combine(bv, bi, v[i], idx[i]);
+    wave_argmax(bv, bi);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    if (l == 0) {
+        sv[w] = bv;
+        si[w] = bi;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < 4; ++k) argmax_combine(bv, bi, sv[k], si[k]);
+        part[row * n_chunks + chunk] = make_float2(bv, __int_as_float(bi));
+    }
+}
+
+// One wavefront per request: reduce each row's chunk records to g[t], then the
+// longest-prefix rule.
+__global__ __launch_bounds__(64) void greedy_decide_kernel(const float2* __restrict__ part,
+                                                           const int32_t* __restrict__ draft,
+                                                           int T, int n_chunks,
+                                                           int32_t* __restrict__ out_tok,
+                                                           int32_t* __restrict__ n_emit) {
+    __shared__ int g[16];
+    const int b = blockIdx.x;
+    const int l = threadIdx.x;
+    for (int t = 0; t < T; ++t) {
+        const float2* rp = part + ((int64_t)b * T + t) * n_chunks;
+        float bv = -INFINITY;
+        int bi = 0x7FFFFFFF;
+        for (int c = l; c < n_chunks; c += 64) argmax_combine(bv, bi, rp[c].x, __float_as_int(rp[c].y));
+        wave_argmax(bv, bi);
+        if (l == 0) g[t] = bi;
+    }
+    __syncthreads();
+    if (l == 0) {
+        const int P = T - 1;
+        const int32_t* d = draft + (int64_t)b * P;
+        int32_t* o = out_tok + (int64_t)b * T;
+        int n = 0;
+        while (n < P && d[n] == g[n]) {
+            o[n] = d[n];
+            ++n;
+        }
+        o[n] = g[n];
+        for (int k = n + 1; k < T; ++k) o[k] = -1;
+        n_emit[b] = n + 1;
+    }
+}
+
+// ================================================================ sampling
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): counter words 0 and 2 are
+// multiplied by two fixed odd constants; high/low product halves are xored with
+// words 1, 3 and the round key; the key advances by two Weyl constants.
+struct Philox4 {
+    uint64_t w[4];
+};
+
+__device__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                 uint64_t k0, uint64_t k1) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += W0;
+            k1 += W1;
+        }
+        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    Philox4 out;
+    out.w[0] = c0;
+    out.w[1] = c1;
+    out.w[2] = c2;
+    out.w[3] = c3;
+    return out;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(
+    const float* __restrict__ logits, int64_t V, int n_chunks, double inv_tau,
+    ChunkStat* __restrict__ stats) {
+    __shared__ float smax[4];
+    __shared__ double ssum[4];
+    const int64_t row = blockIdx.y;
+    const int chunk = blockIdx.x;
+    float v[kPerThread];
+    int idx[kPerThread];
+    load_chunk<VEC>(logits + row * V, V, chunk, v, idx);
+    float m = v[0];
+#pragma unroll
+    for (int i = 1; i < kPerThread; ++i) m = fmaxf(m, v[i]);
+    m = block_max(m, smax);
+    const double md = (double)m;
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i)
+        if (idx[i] != 0x7FFFFFFF) s += exp(((double)v[i] - md) * inv_tau);
+    s = block_sum(s, ssum);
+    if (threadIdx.x == 0) {
+        ChunkStat cs;
+        cs.mass = s;
+        cs.m = m;
+        cs.pad = 0;
+        stats[row * n_chunks + chunk] = cs;
+    }
+}
+
+// Inverse CDF over a row, starting at chunk `c_start` whose preceding mass is
+// `before`: returns the smallest v >= c_start*kChunk with before + sum of
+// weights up to v > target, or -1 if the row ends first.  Weights are
+// exp((l - m) * inv_tau) with token `skip` weighted 0.
+__device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_chunks,
+                                int c_start, double before, double target, double m,
+                                double inv_tau, int skip, double* dscr, int* iscr) {
+    for (int c = c_start; c < n_chunks; ++c) {
+        const int64_t e0 = (int64_t)c * kChunk + (int64_t)threadIdx.x * kPerThread;
+        double w[kPerThread];
+        double own = 0.0;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t e = e0 + j;
+            double x = 0.0;
+            if (e < V && (int)e != skip) x = exp(((double)row[e] - m) * inv_tau);
+            w[j] = x;
+            own += x;
+        }
+        double total;
+        const double excl = block_exclusive_scan(own, dscr, total);
+        int found = 0x7FFFFFFF;
+        double run = before + excl;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            run += w[j];
+            if (found == 0x7FFFFFFF && w[j] > 0.0 && run > target) found = (int)(e0 + j);
+        }
+        found = block_min_int(found, iscr);
+        if (found != 0x7FFFFFFF) return found;
+        before += total;
+    }
+    return -1;
+}
+
+// Largest v with non-zero weight (v != skip): the inverse-CDF fallback when
+// rounding leaves the target beyond the accumulated mass.
+__device__ int last_positive(const float* __restrict__ row, int64_t V, double m, double inv_tau,
+                             int skip, int* iscr) {
+    for (int64_t c0 = ((V - 1) / kChunk) * kChunk; c0 >= 0; c0 -= kChunk) {
+        int best = -1;
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t e = c0 + (int64_t)threadIdx.x * kPerThread + j;
+            if (e < V && (int)e != skip && exp(((double)row[e] - m) * inv_tau) > 0.0) best = (int)e;
+        }
+        best = -block_min_int(-best, iscr);
+        if (best >= 0) return best;
+    }
+    return 0;
+}
+
+__global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ draft,
+    const ChunkStat* __restrict__ stats, int T, int64_t V, int n_chunks, double inv_tau,
+    uint64_t seed, const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0,
+    int32_t* __restrict__ out_tok, int32_t* __restrict__ n_emit) {
+    __shared__ double dscr[4];
+    __shared__ float fscr[4];
+    __shared__ int iscr[4];
+    __shared__ double cum[kVerifyThreads];
+    __shared__ double u_sh[2];
+    const int b = blockIdx.x;
+    const int P = T - 1;
+    const uint64_t rid = request_id[b];
+    const int64_t p0 = pos0[b];
+    int32_t* o = out_tok + (int64_t)b * T;
+    int n = 0;
+    int emitted = -1;
+    for (int s = 1; s <= T && emitted < 0; ++s) {
+        const int t = (s <= P) ? s - 1 : T - 1;
+        const int64_t rowid = (int64_t)b * T + t;
+        const float* row = logits + rowid * V;
+        const ChunkStat* st = stats + rowid * n_chunks;
+        // row maximum and normaliser from the chunk records
+        float mf = -INFINITY;
+        for (int c = threadIdx.x; c < n_chunks; c += kVerifyThreads) mf = fmaxf(mf, st[c].m);
+        mf = block_max(mf, fscr);
+        const double m = (double)mf;
+        double zpart = 0.0;
+        for (int c = threadIdx.x; c < n_chunks; c += kVerifyThreads)
+            zpart += st[c].mass * exp(((double)st[c].m - m) * inv_tau);
+        const double Z = block_sum(zpart, dscr);
+        if (threadIdx.x == 0) {
+            const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
+            u_sh[0] = (double)(r.w[0] >> 11) * 0x1p-53;
+            u_sh[1] = (double)(r.w[1] >> 11) * 0x1p-53;
+        }
+        __syncthreads();
+        const double u_acc = u_sh[0], u_res = u_sh[1];
+        int skip = -1;
+        double target;
+        if (s <= P) {
+            const int d = draft[(int64_t)b * P + (s - 1)];
+            const bool d_ok = d >= 0 && (int64_t)d < V;  // an id outside the vocabulary has p = 0
+            const double ed = d_ok ? exp(((double)row[d] - m) * inv_tau) : 0.0;
+            if (u_acc * Z < ed) {
+                if (threadIdx.x == 0) o[n] = d;
+                ++n;
+                __syncthreads();
+                continue;
+            }
+            skip = d_ok ? d : -1;
+            target = u_res * (Z - ed);
+        } else {
+            target = u_res * Z;
+        }
+        // locate the chunk holding the target from the chunk masses
+        double before = 0.0;
+        int c_hit = -1;
+        for (int c0 = 0; c0 < n_chunks && c_hit < 0; c0 += kVerifyThreads) {
+            const int c = c0 + threadIdx.x;
+            double mass = 0.0;
+            if (c < n_chunks) {
+                mass = st[c].mass * exp(((double)st[c].m - m) * inv_tau);
+                if (skip >= 0 && skip / kChunk == c) mass -= exp(((double)row[skip] - m) * inv_tau);
+            }
+            double total;
+            const double excl = block_exclusive_scan(mass, dscr, total);
+            const int hit = (c < n_chunks && before + excl + mass > target) ? c : 0x7FFFFFFF;
+            const int first = block_min_int(hit, iscr);
+            if (first != 0x7FFFFFFF) {
+                if (c == first) cum[0] = before + excl;
+                __syncthreads();
+                before = cum[0];
+                c_hit = first;
+                __syncthreads();
+            } else {
+                before += total;
+            }
+        }
+        int tok = -1;
+        if (c_hit >= 0)
+            tok = inverse_cdf_from(row, V, n_chunks, c_hit, before, target, m, inv_tau, skip, dscr, iscr);
+        if (tok < 0) tok = last_positive(row, V, m, inv_tau, skip, iscr);
+        emitted = tok;
+    }
+    if (threadIdx.x == 0) {
+        o[n] = emitted;
+        for (int k = n + 1; k < T; ++k) o[k] = -1;
+        n_emit[b] = n + 1;
+    }
+}
+
+// ------------------------------------------------------------------- hosts
+size_t greedy_workspace_bytes(int B, int T, int64_t V) {
+    const int64_t n_chunks = (V + kChunk - 1) / kChunk;
+    return (size_t)B * T * n_chunks * sizeof(float2);
+}
+
+size_t sample_workspace_bytes(int B, int T, int64_t V) {
+    const int64_t n_chunks = (V + kChunk - 1) / kChunk;
+    return (size_t)B * T * n_chunks * sizeof(ChunkStat);
+}
+
+int launch_verify_greedy(const float* logits, const int32_t* draft, int B, int T, int64_t V,
+                         int32_t* out_tok, int32_t* n_emit, void* ws, hipStream_t stream) {
+    const int n_chunks = (int)((V + kChunk - 1) / kChunk);
+    float2* part = reinterpret_cast<float2*>(ws);
+    const dim3 grid(n_chunks, B * T);
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL(greedy_partial_kernel<true>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, part);
+    else
+        hipLaunchKernelGGL(greedy_partial_kernel<false>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, part);
+    int st = launch_status();
+    if (st != DFLASH_OK) return st;
+    hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(64), 0, stream, part, draft, T, n_chunks, out_tok, n_emit);
+    return launch_status();
+}
+
+int launch_verify_sample(const float* logits, const int32_t* draft, int B, int T, int64_t V,
+                         float temperature, uint64_t seed, const uint64_t* request_id,
+                         const int64_t* pos0, int32_t* out_tok, int32_t* n_emit, void* ws,
+                         hipStream_t stream) {
+    const int n_chunks = (int)((V + kChunk - 1) / kChunk);
+    ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws);
+    const double inv_tau = 1.0 / (double)temperature;
+    const dim3 grid(n_chunks, B * T);
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL(sample_stats_kernel<true>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, inv_tau, stats);
+    else
+        hipLaunchKernelGGL(sample_stats_kernel<false>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, inv_tau, stats);
+    int st = launch_status();
+    if (st != DFLASH_OK) return st;
+    hipLaunchKernelGGL(sample_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, logits, draft, stats, T, V,
+                       n_chunks, inv_tau, seed, request_id, pos0, out_tok, n_emit);
+    return launch_status();
+}
+
+}  // namespace dflash

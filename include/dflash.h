@@ -1,0 +1,187 @@
+/*
+ * dflash.h - C ABI of the DFlash 2 cycle-tail library for MI355X (gfx950).
+ *
+ * One draft-verify cycle of DFlash 2 block-parallel speculative decoding ends
+ * with five steps, each one call here:
+ *
+ *   dflash_conv2tap       two-tap dynamic depthwise conv on draft hidden states
+ *   dflash_head_topk      draft LM head fused with per-position top-16 retention
+ *   dflash_select_path    low-rank bilinear pair scores + max-sum path (DP)
+ *   dflash_verify_greedy  greedy longest-prefix acceptance
+ *   dflash_verify_sample  rejection-sampling acceptance (Philox4x64-10 draws)
+ *
+ * Sources (the pages describe the method in words only):
+ *   tamsi.dev, "DFlash 2 - 3x plus de tokens sur Qwen3.8-27B, meme sortie",
+ *     section "L'idee, sans le papier" (top-16 lists, pair selector, two-tap
+ *     conv) and "Les chiffres qui comptent..." (greedy = target exactly,
+ *     rejection sampling keeps the target distribution);
+ *   myaiexp.com, "DFlash 2", section "main features" (path selector over the
+ *     top 16 per position scoring adjacent pairs; two-tap dynamic conv;
+ *     lossless verification);
+ *   latenode.com, "DFlash 2: un drafter de 3.43x que cae a 1.45x bajo carga",
+ *     opening section and FAQ (selector traces one coherent route; lossless);
+ *   postsingularityinstitute.com, "Qwen 3.8 27B + DFlash2: 140 Token/Sec?",
+ *     Resume (candidates chosen by a bilinear attention).
+ *
+ * Conventions shared by every entry point:
+ *   - Array pointers are DEVICE pointers, allocated and owned by the caller,
+ *     row-major and contiguous, 16-byte aligned.  bf16 arrays are passed as
+ *     uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     asynchronously on it; nothing allocates, frees or synchronises.  Outputs
+ *     are valid once the stream reaches them.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns DFLASH_ERR_INVALID (or _UNSUPPORTED / _WORKSPACE) and enqueues
+ *     nothing.  Validation makes no HIP call, so it can be exercised on a host
+ *     without a GPU.
+ *   - Workspace: where a call takes (workspace, workspace_bytes), passing
+ *     workspace == NULL stores the bytes needed in *workspace_bytes and returns
+ *     DFLASH_OK without launching; otherwise *workspace_bytes is the size of
+ *     the caller's buffer and must be at least that.  Contents need no
+ *     initialisation and are scratch after the call.
+ *   - Floating-point inputs must be finite.  Index outputs lie in [0, V).
+ *   - The library keeps no state between calls other than a per-device
+ *     property cache filled on first use.  Calls on different streams may run
+ *     concurrently if their workspaces differ.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    DFLASH_OK = 0,
+    DFLASH_ERR_INVALID = 1,     /* null pointer, bad size, misalignment, aliasing */
+    DFLASH_ERR_UNSUPPORTED = 2, /* a size this library does not implement (K != 16) */
+    DFLASH_ERR_WORKSPACE = 3,   /* workspace smaller than required */
+    DFLASH_ERR_LAUNCH = 4,      /* HIP reported an error when enqueueing */
+    DFLASH_ERR_DEVICE = 5       /* current device is not a gfx950 GPU */
+};
+
+/* Human-readable name of a status code (static string). */
+const char* dflash_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int dflash_version(void);
+
+/*
+ * Two-tap dynamic depthwise causal conv over block slots.
+ * Source: tamsi.dev "DFlash 2 - 3x plus de tokens...", section "L'idee, sans
+ * le papier" (two-tap conv in the Canon / short-conv style around attention
+ * and MLP against suffix decay); myaiexp.com "DFlash 2", main features (two-
+ * tap dynamic convolution).  Reading: per token and per channel taps,
+ *     y[s][t][c] = a[s][t][c] * x[s][t][c] + b[s][t][c] * x[s][t-1][c],
+ *     x[s][-1][c] = 0,  a = taps[s][t][0:D],  b = taps[s][t][D:2D];
+ * the sum is rounded once to float32, then to bf16 (nearest-even).
+ *   x     bf16 [n_seq][T][D]     draft hidden states (one sequence = one block)
+ *   taps  bf16 [n_seq][T][2*D]   per-token taps
+ *   y     bf16 [n_seq][T][D]     output; must not overlap x or taps
+ * Requires n_seq >= 1, 1 <= T <= 16, D >= 8, D % 8 == 0.
+ */
+int dflash_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y,
+                    int64_t n_seq, int32_t T, int32_t D, void* stream);
+
+/*
+ * Draft LM head fused with top-K retention per row.
+ * Source: tamsi.dev, section "L'idee, sans le papier" (the right token is in
+ * the top 16 far more often than at top-1, so 16 candidates are kept);
+ * myaiexp.com "DFlash 2", main features (top 16 per position).
+ *   z[m][v] = sum_d h[m][d] * W[v][d]; per row the K largest z, ordered by
+ *   value descending, ties to the lower vocab id.  The candidates are found
+ *   with a bf16 MFMA GEMM (float32 accumulation) and a running top-16 per row;
+ *   the best 20 of them are then re-scored exactly (float64 dot products,
+ *   in which every bf16 product is exact) and ordered by the exact value, so
+ *   top_val[m][k] = float32 of the exact logit.
+ *   h        bf16 [M][D]     draft hidden states of the draft positions
+ *   W        bf16 [V][D]     LM-head rows (vocab entry v is row v)
+ *   top_val  f32  [M][K]     output values, descending
+ *   top_idx  i32  [M][K]     output vocab ids
+ * Requires M >= 1, D >= 8, D % 8 == 0, V >= K; K == 16 (else UNSUPPORTED).
+ * Workspace: partial candidate lists, see the workspace convention above.
+ */
+int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
+                     int64_t V, int32_t K, float* top_val, int32_t* top_idx,
+                     void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Pair selector: one coherent path through the P x K candidate lattice.
+ * Source: tamsi.dev, section "L'idee, sans le papier" (a pair selector of
+ * about 2 M parameters chooses a coherent path among good candidates);
+ * myaiexp.com "DFlash 2", main features (adjacent pairs scored);
+ * postsingularityinstitute.com, Resume (bilinear attention over candidates).
+ * Reading: pair(c, c') = <feat_l[c], feat_r[c']> with low-rank tables
+ * feat_l = E P^T, feat_r = E Q^T ([V][r] float32, prepared by the caller once
+ * per weight load); max-sum DP
+ *     delta_0[i] = val[0][i],
+ *     delta_{p+1}[j] = val[p+1][j] + max_i (delta_p[i] + pair_p[i][j]),
+ * lowest i on ties, path ending at the lowest maximiser of delta_{P-1}.
+ * Pair sums run over k = 0..r-1 in order and the DP in float64.
+ *   top_val    f32 [B][P][K]   candidate draft logits (from dflash_head_topk)
+ *   top_idx    i32 [B][P][K]   candidate vocab ids, each in [0, V)
+ *   feat_l/r   f32 [V][r]
+ *   path_rank  i32 [B][P]      chosen candidate rank per position
+ *   path_tok   i32 [B][P]      chosen vocab id per position (the draft tokens)
+ *   path_score f32 [B]         float32 of the path's float64 score
+ * Requires B >= 1, 1 <= P <= 15, V >= 1, 1 <= r <= 1024, r % 4 == 0;
+ * K == 16 (else UNSUPPORTED).
+ */
+int dflash_select_path(const float* top_val, const int32_t* top_idx,
+                       const float* feat_l, const float* feat_r,
+                       int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
+                       int32_t* path_rank, int32_t* path_tok, float* path_score,
+                       void* stream);
+
+/*
+ * Greedy verification.
+ * Source: tamsi.dev, section "Les chiffres qui comptent..." (greedy output is
+ * exactly the target's); latenode.com, section "El desacuerdo empieza..."
+ * (acceptance length = tokens completed per verify step).
+ * Block of T slots: slot 0 is the last verified token, slot s = 1..T-1 holds
+ * draft[b][s-1]; target row t is the distribution after slot t.
+ * g[t] = argmax_v logits[b][t][v] (lowest v on ties); n = length of the
+ * longest prefix with draft[b][s-1] == g[s-1]; out_tok[b][0..n-1] = drafts,
+ * out_tok[b][n] = g[n], -1 after; n_emit[b] = n + 1.
+ *   logits  f32 [B][T][V]   target block logits
+ *   draft   i32 [B][T-1]
+ *   out_tok i32 [B][T], n_emit i32 [B]
+ * Requires B >= 1, 2 <= T <= 16, V >= 1, V < 2^31.
+ */
+int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B,
+                         int32_t T, int64_t V, int32_t* out_tok, int32_t* n_emit,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification with a deterministic draft.
+ * Source: tamsi.dev, section "Les chiffres qui comptent..." (sampling through
+ * rejection sampling keeps the target distribution); latenode.com FAQ (same).
+ * p_t(v) = e_t(v) / Z_t, e_t(v) = exp((l_t(v) - max_v l_t) * (1/tau)), float64.
+ * For slot s = 1..T-1 with d = draft[b][s-1]: accept iff u_acc * Z_{s-1} <
+ * e_{s-1}(d).  On the first rejection emit the smallest v with
+ * sum_{w<=v, w!=d} e(w) > u_res * (Z - e(d)) (the residual max(0, p - q),
+ * q = one-hot(d)) and stop; if every draft is accepted emit the bonus: the
+ * smallest v with sum_{w<=v} e_{T-1}(w) > u_res * Z_{T-1}.
+ * Uniforms for the slot s being decided (s = T for the bonus):
+ * (w0, w1, w2, w3) = Philox4x64-10(counter = (1, request_id[b], pos0[b] + s, 0),
+ * key = (seed, 0)) [Salmon et al., SC'11]; u_acc = (w0 >> 11) * 2^-53,
+ * u_res = (w1 >> 11) * 2^-53.  Draws depend on (seed, request id, position)
+ * only, so a request's outcome is the same in any batch.
+ *   request_id u64 [B], pos0 i64 [B] (absolute position of slot 0)
+ *   outputs as for dflash_verify_greedy.
+ * Requires B >= 1, 2 <= T <= 16, 1 <= V < 2^31, temperature finite and > 0.
+ */
+int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B,
+                         int32_t T, int64_t V, float temperature, uint64_t seed,
+                         const uint64_t* request_id, const int64_t* pos0,
+                         int32_t* out_tok, int32_t* n_emit,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H */

@@ -25,3 +25,16 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(scope="session")
+def dev():
+    import torch
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="session")
+def dfl():
+    import block_draft_verification_amd as m
+    m.lib()
+    return m

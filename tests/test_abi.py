@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+declared in include/dflash.h, shares torch's HIP runtime, and rejects bad
+arguments before any HIP call (a fully valid call on a GPU-less host fails
+with DFLASH_ERR_DEVICE instead of falling back to anything)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import block_draft_verification_amd as dfl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH, DEVICE = 0, 1, 2, 3, 4, 5
+
+needs_lib = pytest.mark.skipif(not os.path.exists(dfl.LIB_PATH), reason="libdflash.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(dflash_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_five_steps():
+    names = declared_functions()
+    for n in ("dflash_conv2tap", "dflash_head_topk", "dflash_select_path",
+              "dflash_verify_greedy", "dflash_verify_sample"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    L = dfl.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) == set(dfl.EXPORTS)
+    assert dfl.status_string(WORKSPACE) == "workspace too small"
+    assert L.dflash_version() >> 16 == 1
+
+
+@needs_lib
+def test_single_hip_runtime_in_process():
+    dfl.lib()
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(paths) == 1, paths
+
+
+# fake, 256-byte aligned, non-overlapping device addresses for validation tests
+A = [ctypes.c_void_p((i + 1) << 40) for i in range(16)]
+NULL = None
+
+
+def ws_query(fn, *before, after=(None,)):
+    n = ctypes.c_size_t(0)
+    st = fn(*before, NULL, ctypes.byref(n), *after)
+    return st, n.value
+
+
+@needs_lib
+def test_conv_validation():
+    f = dfl.lib().dflash_conv2tap
+    assert f(NULL, A[1], A[2], 1, 8, 64, NULL) == INVALID
+    assert f(A[0], A[1], A[2], 0, 8, 64, NULL) == INVALID          # n_seq
+    assert f(A[0], A[1], A[2], 1, 17, 64, NULL) == INVALID         # T > 16
+    assert f(A[0], A[1], A[2], 1, 8, 60, NULL) == INVALID          # D % 8
+    assert f(A[0], A[1], A[0], 1, 8, 64, NULL) == INVALID          # y == x
+    assert f(A[0], A[1], ctypes.c_void_p((1 << 40) + 8), 1, 8, 64, NULL) == INVALID  # overlap
+    assert f(ctypes.c_void_p((1 << 40) + 8), A[1], A[2], 1, 8, 64, NULL) == INVALID  # misaligned
+    if not torch.cuda.is_available():
+        assert f(A[0], A[1], A[2], 1, 8, 64, NULL) == DEVICE
+
+
+@needs_lib
+def test_head_validation_and_workspace():
+    f = dfl.lib().dflash_head_topk
+    st, need = ws_query(f, A[0], A[1], 7, 5120, 151936, 16, A[2], A[3])
+    assert st == OK and need >= 7 * 16 * 8
+    st2, need2 = ws_query(f, A[0], A[1], 480, 5120, 262144, 16, A[2], A[3])
+    assert st2 == OK and need2 > need
+    assert ws_query(f, A[0], A[1], 7, 5120, 151936, 8, A[2], A[3])[0] == UNSUPPORTED
+    assert ws_query(f, A[0], A[1], 7, 5120, 15, 16, A[2], A[3])[0] == INVALID     # V < K
+    assert ws_query(f, A[0], A[1], 0, 5120, 4096, 16, A[2], A[3])[0] == INVALID
+    assert ws_query(f, A[0], A[1], 7, 5121, 4096, 16, A[2], A[3])[0] == INVALID
+    assert ws_query(f, NULL, A[1], 7, 256, 4096, 16, A[2], A[3])[0] == INVALID
+    small = ctypes.c_size_t(need - 1)
+    assert f(A[0], A[1], 7, 5120, 151936, 16, A[2], A[3], A[4], ctypes.byref(small), NULL) == WORKSPACE
+    assert f(A[0], A[1], 7, 5120, 151936, 16, A[2], A[3], A[4], NULL, NULL) == INVALID
+    ok = ctypes.c_size_t(need)
+    # output aliasing the input hidden states
+    assert f(A[0], A[1], 7, 5120, 151936, 16, A[0], A[3], A[4], ctypes.byref(ok), NULL) == INVALID
+    if not torch.cuda.is_available():
+        assert f(A[0], A[1], 7, 5120, 151936, 16, A[2], A[3], A[4], ctypes.byref(ok), NULL) == DEVICE
+
+
+@needs_lib
+def test_select_validation():
+    f = dfl.lib().dflash_select_path
+    args = lambda B, P, K, V, r, out0=A[4]: (A[0], A[1], A[2], A[3], B, P, K, V, r, out0, A[5], A[6], NULL)
+    assert f(*args(1, 7, 8, 4096, 32)) == UNSUPPORTED
+    assert f(*args(1, 16, 16, 4096, 32)) == INVALID
+    assert f(*args(1, 0, 16, 4096, 32)) == INVALID
+    assert f(*args(1, 7, 16, 4096, 30)) == INVALID
+    assert f(*args(1, 7, 16, 4096, 512)) == INVALID
+    assert f(*args(1, 7, 16, 4096, 32, out0=A[0])) == INVALID
+    if not torch.cuda.is_available():
+        assert f(*args(2, 7, 16, 4096, 192)) == DEVICE
+
+
+@needs_lib
+def test_verify_validation():
+    g = dfl.lib().dflash_verify_greedy
+    s = dfl.lib().dflash_verify_sample
+    st, need = ws_query(g, A[0], A[1], 1, 8, 151936, A[2], A[3])
+    assert st == OK and need > 0
+    assert ws_query(g, A[0], A[1], 1, 1, 100, A[2], A[3])[0] == INVALID     # T < 2
+    assert ws_query(g, A[0], A[1], 1, 17, 100, A[2], A[3])[0] == INVALID
+    assert ws_query(g, A[0], A[1], 1, 8, 100, A[0], A[3])[0] == INVALID     # out aliases logits
+    st, need_s = ws_query(s, A[0], A[1], 8, 8, 151936, 1.0, 0, A[4], A[5], A[2], A[3])
+    assert st == OK and need_s > 0
+    for bad_tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert ws_query(s, A[0], A[1], 8, 8, 100, bad_tau, 0, A[4], A[5], A[2], A[3])[0] == INVALID
+    assert ws_query(s, A[0], A[1], 8, 8, 100, 1.0, 0, NULL, A[5], A[2], A[3])[0] == INVALID
+    small = ctypes.c_size_t(need_s - 1)
+    assert s(A[0], A[1], 8, 8, 151936, 1.0, 0, A[4], A[5], A[2], A[3], A[6], ctypes.byref(small),
+             NULL) == WORKSPACE
+    if not torch.cuda.is_available():
+        ok = ctypes.c_size_t(need)
+        assert g(A[0], A[1], 1, 8, 151936, A[2], A[3], A[6], ctypes.byref(ok), NULL) == DEVICE
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(dfl.DFlashError):
+        dfl.conv2tap(x, torch.zeros(1, 8, 128, dtype=torch.bfloat16))

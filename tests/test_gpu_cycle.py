@@ -1,0 +1,105 @@
+"""End-to-end cycle on the GPU against the oracle: the tiny configuration
+generator -> GPU vs generator -> oracle, a stage-wise check at batch 8, and
+bit-identical reruns."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.cycle import run_cycle
+from oracle.head import head_topk as oracle_topk
+from oracle.selector import select_path as oracle_select
+from oracle.verify import verify_greedy as og, verify_sample as osamp
+from workload import get_config, make_cycle_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_cycle(dfl, inp, cfg):
+    B, T, P = cfg.B, cfg.T, cfg.P
+    ys = [dfl.conv2tap(inp["x"][l], inp["taps"][l]) for l in range(cfg.L)]
+    tv, ti = dfl.head_topk(inp["h"], inp["W"])
+    rank, tok, score = dfl.select_path(tv.view(B, P, 16), ti.view(B, P, 16), inp["F_l"], inp["F_r"])
+    g = {"greedy": B, "sample": 0, "mixed": B // 2}[cfg.verify]
+    out = torch.empty((B, T), dtype=torch.int32, device=tok.device)
+    n = torch.empty((B,), dtype=torch.int32, device=tok.device)
+    if g > 0:
+        out[:g], n[:g] = dfl.verify_greedy(inp["target"][:g].contiguous(), tok[:g].contiguous())
+    if g < B:
+        o2, n2 = dfl.verify_sample(inp["target"][g:].contiguous(), tok[g:].contiguous(), inp["temperature"],
+                                   inp["seed"], inp["request_id"][g:].contiguous(), inp["pos0"][g:].contiguous())
+        out[g:], n[g:] = o2, n2
+    torch.cuda.synchronize()
+    return {"y": ys, "top_val": tv.view(B, P, 16), "top_idx": ti.view(B, P, 16), "path_rank": rank,
+            "path_tok": tok, "path_score": score, "out_tok": out, "n_emit": n}
+
+
+def to_dev(inp, dev):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def test_tiny_config_end_to_end(dfl, dev):
+    cfg = get_config("c1_tiny")
+    inp = make_cycle_inputs(cfg)
+    res = gpu_cycle(dfl, to_dev(inp, dev), cfg)
+    ref = run_cycle(inp, cfg.B, cfg.T)
+    for l in range(cfg.L):
+        assert torch.equal(res["y"][l].cpu().view(torch.int16), ref["y"][l].view(torch.int16))
+    assert np.array_equal(res["top_idx"].cpu().numpy(), ref["top_idx"])
+    assert np.array_equal(res["top_val"].cpu().numpy(), ref["top_val"])
+    for k in ("path_rank", "path_tok", "path_score", "out_tok", "n_emit"):
+        assert np.array_equal(res[k].cpu().numpy(), ref[k]), k
+
+
+@pytest.mark.parametrize("name", ["c1_tiny"])
+def test_tiny_variants_mixed_and_sampled(dfl, dev, name):
+    for verify, B in (("mixed", 6), ("sample", 3)):
+        cfg = get_config(name, name=f"{name}_{verify}", B=B, verify=verify, plant_alpha=3.0)
+        inp = make_cycle_inputs(cfg)
+        res = gpu_cycle(dfl, to_dev(inp, dev), cfg)
+        ref = run_cycle(inp, cfg.B, cfg.T, verify=verify)
+        for k in ("top_idx", "path_tok", "out_tok", "n_emit"):
+            assert np.array_equal(res[k].cpu().numpy(), ref[k]), (verify, k)
+
+
+def test_stagewise_batch8_sampled(dfl, dev):
+    """Batch 8 at the full shapes (D 5120, V 151936), sampling at tau = 1:
+    each GPU stage is checked against the oracle fed the GPU's previous stage."""
+    cfg = get_config("c3_b8")
+    inp = make_cycle_inputs(cfg, device=dev)
+    res = gpu_cycle(dfl, inp, cfg)
+    rows = [0, 13, 55]
+    rv, ri, _ = oracle_topk(inp["h"].cpu(), inp["W"].cpu(), rows=rows)
+    assert np.array_equal(res["top_idx"].view(-1, 16).cpu().numpy()[rows], ri)
+    assert np.array_equal(res["top_val"].view(-1, 16).cpu().numpy()[rows], rv)
+    r0, t0, s0, _ = oracle_select(res["top_val"].cpu().numpy(), res["top_idx"].cpu().numpy(),
+                                  inp["F_l"].cpu(), inp["F_r"].cpu())
+    assert np.array_equal(res["path_tok"].cpu().numpy(), t0)
+    assert np.array_equal(res["path_score"].cpu().numpy(), s0)
+    o0, n0 = osamp(inp["target"].cpu(), res["path_tok"].cpu(), cfg.temperature, cfg.seed,
+                   inp["request_id"].cpu(), inp["pos0"].cpu())
+    assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
+    assert np.array_equal(res["n_emit"].cpu().numpy(), n0)
+
+
+def test_stagewise_batch1_greedy_acceptance(dfl, dev):
+    cfg = get_config("c2_b1")
+    inp = make_cycle_inputs(cfg, device=dev)
+    res = gpu_cycle(dfl, inp, cfg)
+    rv, ri, _ = oracle_topk(inp["h"].cpu(), inp["W"].cpu())
+    assert np.array_equal(res["top_idx"].view(-1, 16).cpu().numpy(), ri)
+    o0, n0 = og(inp["target"].cpu(), res["path_tok"].cpu())
+    assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
+    assert np.array_equal(res["n_emit"].cpu().numpy(), n0)
+    # planted margin: the drafted tokens are (almost always) the planted ones
+    same = res["path_tok"].view(-1).cpu().numpy() == inp["planted"].cpu().numpy()
+    assert same.sum() >= cfg.M - 1
+
+
+def test_reruns_bit_identical(dfl, dev):
+    cfg = get_config("c4_b32", name="c4_small", D=512, V=20000, r=32)
+    inp = make_cycle_inputs(cfg, device=dev)
+    a = gpu_cycle(dfl, inp, cfg)
+    b = gpu_cycle(dfl, inp, cfg)
+    for k in ("top_val", "top_idx", "path_rank", "path_score", "out_tok", "n_emit"):
+        assert torch.equal(a[k], b[k]), k
