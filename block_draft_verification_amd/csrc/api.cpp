@@ -132,7 +132,7 @@ int dflash_select_path(const float* top_val, const int32_t* top_idx, const float
         return DFLASH_ERR_INVALID;
     if (B < 1 || P < 1 || P > 15 || V < 1 || r < 4 || r > 256 || r % 4 != 0) return DFLASH_ERR_INVALID;
     if (K != 16) return DFLASH_ERR_UNSUPPORTED;
-    if (!aligned4(top_val) || !aligned4(top_idx) || !aligned4(feat_l) || !aligned4(feat_r) ||
+    if (!aligned4(top_val) || !aligned4(top_idx) || !aligned16(feat_l) || !aligned16(feat_r) ||
         !aligned4(path_rank) || !aligned4(path_tok) || !aligned4(path_score))
         return DFLASH_ERR_INVALID;
     const size_t nbp = (size_t)B * P * 4, nin = (size_t)B * P * K * 4;

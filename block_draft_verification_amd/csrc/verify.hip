@@ -185,26 +185,28 @@ __global__ __launch_bounds__(kVerifyThreads) void greedy_partial_kernel(
     }
 }
 
-// One wavefront per request: reduce each row's chunk records to g[t], then the
-// longest-prefix rule.
-__global__ __launch_bounds__(64) void greedy_decide_kernel(const float2* __restrict__ part,
-                                                           const int32_t* __restrict__ draft,
-                                                           int T, int n_chunks,
-                                                           int32_t* __restrict__ out_tok,
-                                                           int32_t* __restrict__ n_emit) {
+// One workgroup per request, one wavefront per row (T wavefronts): reduce the
+// row's chunk records to g[t]; then one lane applies the longest-prefix rule.
+__global__ __launch_bounds__(1024) void greedy_decide_kernel(const float2* __restrict__ part,
+                                                             const int32_t* __restrict__ draft,
+                                                             int T, int n_chunks,
+                                                             int32_t* __restrict__ out_tok,
+                                                             int32_t* __restrict__ n_emit) {
     __shared__ int g[16];
     const int b = blockIdx.x;
-    const int l = threadIdx.x;
-    for (int t = 0; t < T; ++t) {
-        const float2* rp = part + ((int64_t)b * T + t) * n_chunks;
-        float bv = -INFINITY;
-        int bi = 0x7FFFFFFF;
-        for (int c = l; c < n_chunks; c += 64) argmax_combine(bv, bi, rp[c].x, __float_as_int(rp[c].y));
-        wave_argmax(bv, bi);
-        if (l == 0) g[t] = bi;
+    const int t = threadIdx.x >> 6;
+    const int l = threadIdx.x & 63;
+    const float2* rp = part + ((int64_t)b * T + t) * n_chunks;
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int c = l; c < n_chunks; c += 64) {
+        const float2 e = rp[c];
+        argmax_combine(bv, bi, e.x, __float_as_int(e.y));
     }
+    wave_argmax(bv, bi);
+    if (l == 0) g[t] = bi;
     __syncthreads();
-    if (l == 0) {
+    if (threadIdx.x == 0) {
         const int P = T - 1;
         const int32_t* d = draft + (int64_t)b * P;
         int32_t* o = out_tok + (int64_t)b * T;
@@ -449,7 +451,8 @@ int launch_verify_greedy(const float* logits, const int32_t* draft, int B, int T
         hipLaunchKernelGGL(greedy_partial_kernel<false>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, part);
     int st = launch_status();
     if (st != DFLASH_OK) return st;
-    hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(64), 0, stream, part, draft, T, n_chunks, out_tok, n_emit);
+    hipLaunchKernelGGL(greedy_decide_kernel, dim3(B), dim3(64 * T), 0, stream, part, draft, T, n_chunks, out_tok,
+                       n_emit);
     return launch_status();
 }
 

@@ -61,11 +61,26 @@ def test_vocab_exactly_k_and_constant_rows(dfl, dev):
 
 
 def test_increasing_logits_stress_candidate_overflow(dfl, dev):
-    """Logits increase along the vocabulary: every element beats the running
-    threshold, which exercises the bounded candidate buffers' retry path."""
+    """Strictly increasing logits z[v] = v / 256 (exact: W[v] = (v // 256,
+    v % 256), h = (1, 1/256)): every element beats the running threshold, which
+    exercises the bounded candidate buffers' retry path."""
     V, D = 6000, 16
     W = torch.zeros(V, D)
-    W[:, 0] = torch.arange(V, dtype=torch.float32) / 64.0  # bf16-exact up to 256
+    v = torch.arange(V)
+    W[:, 0] = (v // 256).float()
+    W[:, 1] = (v % 256).float()
+    h = torch.zeros(3, D)
+    h[:, 0] = 1.0
+    h[:, 1] = 1.0 / 256
+    check(dfl, dev, h.to(torch.bfloat16), W.to(torch.bfloat16))
+
+
+def test_rounded_ramp_heavy_ties(dfl, dev):
+    """A ramp rounded to bf16 (v / 64): long runs of equal logits at the top,
+    so the lower ids must win among equals across strips and retries."""
+    V, D = 6000, 16
+    W = torch.zeros(V, D)
+    W[:, 0] = torch.arange(V, dtype=torch.float32) / 64.0
     h = torch.zeros(3, D)
     h[:, 0] = 1.0
     check(dfl, dev, h.to(torch.bfloat16), W.to(torch.bfloat16))
