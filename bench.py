@@ -71,6 +71,7 @@ class CycleRunner:
         self.g = g
         u8 = torch.uint8
         self.ws_head = torch.empty(dfl.workspace_bytes("head_topk", cfg.M, cfg.D, cfg.V), dtype=u8, device=dev)
+        self.ws_sel = torch.empty(dfl.workspace_bytes("select_path", B, P), dtype=u8, device=dev)
         self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
         self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
                                 device=dev)
@@ -79,7 +80,7 @@ class CycleRunner:
         for s in sets:
             conv = [dfl.bind_conv2tap(s["x"][l], s["taps"][l], self.y[l]) for l in range(L)]
             head = dfl.bind_head_topk(s["h"], W, self.tv, self.ti, self.ws_head)
-            sel = dfl.bind_select_path(tv3, ti3, F_l, F_r, self.rank, self.tok, self.score)
+            sel = dfl.bind_select_path(tv3, ti3, F_l, F_r, self.rank, self.tok, self.score, self.ws_sel)
             ver = []
             if g > 0:
                 ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))

@@ -30,7 +30,7 @@ _SIGNATURES = {
     "dflash_conv2tap": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
     "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
     "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
-                                          _p, _p, _p, _p]),
+                                          _p, _p, _p, _p, _psz, _p]),
     "dflash_verify_greedy": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _p, _p, _p, _psz, _p]),
     "dflash_verify_sample": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p, _p,
                                             _p, _p, _p, _psz, _p]),
@@ -134,7 +134,7 @@ def head_topk(h, W, K=16, workspace=None, out=None):
     return tv, ti
 
 
-def select_path(top_val, top_idx, F_l, F_r, out=None):
+def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None):
     """top_val f32 [B][P][16], top_idx i32 [B][P][16], F_l/F_r f32 [V][r]
     -> (path_rank i32 [B][P], path_tok i32 [B][P], path_score f32 [B])."""
     _need(top_val, torch.float32, "top_val", 3)
@@ -151,8 +151,12 @@ def select_path(top_val, top_idx, F_l, F_r, out=None):
         score = torch.empty((B,), dtype=torch.float32, device=top_val.device)
     else:
         rank, tok, score = out
-    _check(lib().dflash_select_path(_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r,
-                                    _ptr(rank), _ptr(tok), _ptr(score), _stream(top_val.device)),
+    L = lib()
+    before = (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
+              _ptr(score))
+    ws, nbytes = _workspace(L.dflash_select_path, before, (_stream(top_val.device),), top_val.device,
+                            workspace)
+    _check(L.dflash_select_path(*before, _ptr(ws), ctypes.byref(nbytes), _stream(top_val.device)),
            "dflash_select_path")
     return rank, tok, score
 
@@ -237,12 +241,14 @@ def bind_head_topk(h, W, top_val, top_idx, workspace):
                    _ptr(workspace), ctypes.byref(nbytes), _stream(h.device)), "dflash_head_topk")
 
 
-def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score):
+def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score, workspace):
     B, P, K = top_val.shape
     V, r = F_l.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_select_path,
                   (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
-                   _ptr(score), _stream(top_val.device)), "dflash_select_path")
+                   _ptr(score), _ptr(workspace), ctypes.byref(nbytes), _stream(top_val.device)),
+                  "dflash_select_path")
 
 
 def bind_verify_greedy(logits, draft, out_tok, n_emit, workspace):
@@ -264,13 +270,18 @@ def bind_verify_sample(logits, draft, temperature, seed, request_id, pos0, out_t
 
 def workspace_bytes(op, *shape_args):
     """Workspace size of an entry point for the given sizes, without a GPU call:
-    op in {"head_topk": (M, D, V), "verify_greedy": (B, T, V), "verify_sample": (B, T, V)}."""
+    op in {"head_topk": (M, D, V), "select_path": (B, P), "verify_greedy": (B, T, V),
+    "verify_sample": (B, T, V)}."""
     L = lib()
     n = ctypes.c_size_t(0)
     fake = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
     if op == "head_topk":
         M, D, V = shape_args
         code = L.dflash_head_topk(fake[0], fake[1], M, D, V, 16, fake[2], fake[3], None, ctypes.byref(n), None)
+    elif op == "select_path":
+        B, P = shape_args
+        code = L.dflash_select_path(fake[0], fake[1], fake[2], fake[3], B, P, 16, 1024, 16, fake[4], fake[5],
+                                    fake[6], None, ctypes.byref(n), None)
     elif op == "verify_greedy":
         B, T, V = shape_args
         code = L.dflash_verify_greedy(fake[0], fake[1], B, T, V, fake[2], fake[3], None, ctypes.byref(n), None)

@@ -16,7 +16,8 @@ int launch_head_topk(const uint16_t*, const uint16_t*, int64_t, int, int64_t, fl
                      hipStream_t);
 size_t head_workspace_bytes(int64_t M, int64_t V);
 int launch_select_path(const float*, const int32_t*, const float*, const float*, int, int, int64_t, int,
-                       int32_t*, int32_t*, float*, hipStream_t);
+                       int32_t*, int32_t*, float*, void*, hipStream_t);
+size_t select_workspace_bytes(int B, int P);
 size_t greedy_workspace_bytes(int B, int T, int64_t V);
 size_t sample_workspace_bytes(int B, int T, int64_t V);
 int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
@@ -127,7 +128,8 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
 
 int dflash_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
                        const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
-                       int32_t* path_rank, int32_t* path_tok, float* path_score, void* stream) {
+                       int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
+                       size_t* workspace_bytes, void* stream) {
     if (!top_val || !top_idx || !feat_l || !feat_r || !path_rank || !path_tok || !path_score)
         return DFLASH_ERR_INVALID;
     if (B < 1 || P < 1 || P > 15 || V < 1 || r < 4 || r > 256 || r % 4 != 0) return DFLASH_ERR_INVALID;
@@ -146,10 +148,18 @@ int dflash_select_path(const float* top_val, const int32_t* top_idx, const float
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outn[i], outs[j], outn[j])) return DFLASH_ERR_INVALID;
     }
-    int st = check_device();
+    bool query = false;
+    int st = workspace_check(workspace, workspace_bytes, select_workspace_bytes(B, P), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    for (int j = 0; j < 4; ++j)
+        if (overlap(workspace, nws, ins[j], inn[j])) return DFLASH_ERR_INVALID;
+    for (int i = 0; i < 3; ++i)
+        if (overlap(workspace, nws, outs[i], outn[i])) return DFLASH_ERR_INVALID;
+    st = check_device();
     if (st != DFLASH_OK) return st;
     return launch_select_path(top_val, top_idx, feat_l, feat_r, B, P, V, r, path_rank, path_tok, path_score,
-                              (hipStream_t)stream);
+                              workspace, (hipStream_t)stream);
 }
 
 static int verify_common_checks(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,

@@ -24,13 +24,14 @@
 //   from there, and keeps its own running top-16 per row in LDS.  No barrier
 //   inside the stream.  At the end the four wavefronts of a workgroup merge
 //   their lists.
-// * head_wide_kernel (M > 16): a workgroup of WM x WN wavefronts owns an
-//   M-block of 16*MW*WM rows of h and a contiguous range of vocabulary strips
-//   of 16*NT*WN rows.  Per chunk of the hidden dimension, h is staged once in
-//   LDS for all wavefronts, and W goes straight to registers, one chunk
-//   ahead; wavefronts with the same N-group load the same W rows (shared
-//   through L1).  The M-blocks of one strip range are dispatched next to each
-//   other on the same XCD so that they share W through its L2.
+// * head_wide_kernel (M > 16): a workgroup of 2 x WN wavefronts owns an
+//   M-block of 32*MW rows of h and a contiguous range of vocabulary tiles,
+//   walked in strips of 16*NT*WN rows.  Per chunk of the hidden dimension the
+//   whole workgroup stages the h rows and the strip's W rows in LDS
+//   (row-contiguous buffer loads, several chunks ahead in registers) and every
+//   wavefront multiplies its 16*MW x 16*NT tile from there.  The M-blocks of
+//   one range are dispatched next to each other on the same XCD so that they
+//   share W through its L2.
 // * The top-16 epilogue: after a tile, the float32 logits still in the
 //   accumulators are compared with each row's running 16th-best entry (value,
 //   then id); the few survivors go to a bounded per-row buffer and are merged
@@ -40,12 +41,14 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 
 namespace dflash {
 
 constexpr int kCap = 16;        // candidate slots per row between merges
+static_assert(kCap == 16, "one buffered candidate per lane of a 16-lane row");
 constexpr int kRescore = 20;    // float32 candidates re-scored exactly per row
 constexpr int kMergeThreads = 64 * (kRescore / 2);  // one wavefront per two re-scored candidates
 
@@ -107,16 +110,89 @@ __device__ __forceinline__ void topk_init(TopkRows t, int rows, int tid, int nth
     }
 }
 
+// 64-bit key ordered like ranks_before: larger value first, then lower id
+// (-0 counts as +0, as in the float comparison).
+__device__ __forceinline__ uint64_t rank_key(float v, int i) {
+    uint32_t u = __float_as_uint(v == 0.0f ? 0.0f : v);
+    u ^= (u >> 31) ? 0xFFFFFFFFu : 0x80000000u;  // order-preserving map of floats to uint32
+    return ((uint64_t)u << 32) | (uint32_t)(0x7FFFFFFF - i);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __uint_as_float((u >> 31) ? (u ^ 0x80000000u) : ~u);
+}
+__device__ __forceinline__ int key_id(uint64_t k) { return 0x7FFFFFFF - (int)(uint32_t)k; }
+constexpr uint64_t kEmptyKey = 0x007FFFFF00000000ull;  // rank_key(-inf, 0x7FFFFFFF)
+
+// A 64-bit value from another lane of the same 16-lane row (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t xor4_u64(uint64_t x) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, 4);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), 4);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Compare-exchange with the partner's key p: keep the larger key if keep_max.
+__device__ __forceinline__ uint64_t cx(uint64_t k, uint64_t p, bool keep_max) {
+    return ((p > k) == keep_max) ? p : k;
+}
+// DPP controls: quad_perm [1,0,3,2] / [2,3,0,1] / [3,2,1,0] (lane ^ 1, ^ 2, ^ 3),
+// row_half_mirror (^ 7), row_mirror (^ 15), row_ror:8 (^ 8).
+constexpr int kDppX1 = 0xB1, kDppX2 = 0x4E, kDppX3 = 0x1B, kDppX7 = 0x141, kDppX15 = 0x140, kDppX8 = 0x128;
+
+// Bitonic sort of one key per lane over each 16-lane row, descending if DESC.
+// Every merge stage starts with the mirrored comparison (lane ^ (2s - 1)) so
+// all blocks sort in the same direction; only lane ^ 4 needs a permute.
+template <bool DESC>
+__device__ __forceinline__ uint64_t sort16(uint64_t k, int li) {
+    k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX3>(k), ((li & 2) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX7>(k), ((li & 4) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX2>(k), ((li & 2) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX15>(k), ((li & 8) == 0) == DESC);
+    k = cx(k, xor4_u64(k), ((li & 4) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX2>(k), ((li & 2) == 0) == DESC);
+    k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
+    return k;
+}
+// Sort a bitonic sequence of 16 keys (one per lane of a row) descending.
+__device__ __forceinline__ uint64_t merge16_desc(uint64_t k, int li) {
+    k = cx(k, dpp_u64<kDppX8>(k), (li & 8) == 0);
+    k = cx(k, xor4_u64(k), (li & 4) == 0);
+    k = cx(k, dpp_u64<kDppX2>(k), (li & 2) == 0);
+    k = cx(k, dpp_u64<kDppX1>(k), (li & 1) == 0);
+    return k;
+}
+
 // Filter an MW x NT block of 16x16 accumulator tiles into the rows' lists.
 //   rbase: LDS row of the block's first row; grow0: its global row
-//   col0: global vocabulary id of tile column 0 (lane r = 0)
-//   merge rows [0, n_merge_rows) by half-wavefronts h = hw0, hw0 + hw_step, ...
+//   col0: global vocabulary id of fragment 0's column 0; fragment nt starts
+//         col_step ids further on
+//   merge rows [0, n_merge_rows) by 16-lane rows of wavefronts: row group
+//   g = q0, q0 + q_step, ... (lane >> 4 is the group within a wavefront)
+// Candidates (ranking before the row's 16th-best entry) go to a kCap-slot
+// buffer; each row with candidates then sorts them ascending across 16 lanes,
+// takes the lane-wise maximum with its descending list (the top 16 of both,
+// as a bitonic sequence) and sorts that descending.  Candidates that found
+// the buffer full are retried in another round.
 // WG = true: state shared by the workgroup (barriers); false: wave-private.
 template <int MW, int NT, bool WG>
 __device__ __forceinline__ void topk_epilogue(const floatx4 (&acc)[MW][NT], TopkRows t, int rbase, int64_t grow0,
-                              int64_t M, int64_t col0, int nt_act, int64_t V, int mw_act,
-                              int n_merge_rows, int hw0, int hw_step) {
-    const int lane = threadIdx.x & 63;
+                              int64_t M, int64_t col0, int col_step, int nt_act, int64_t V, int mw_act,
+                              int n_merge_rows, int q0, int q_step) {
+    // The empty asm statements make lane, M and rbase opaque at each call, so
+    // that nothing derived from them is hoisted out of the caller's tile loop
+    // (where it would stay live through the streaming loop and spill).
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+    asm volatile("" : "+s"(M));
+    asm volatile("" : "+v"(rbase));
     const int ln = lane & 15, lg = lane >> 4;
     uint32_t pending[MW];
 #pragma unroll
@@ -133,7 +209,7 @@ __device__ __forceinline__ void topk_epilogue(const floatx4 (&acc)[MW][NT], Topk
                 const int iq[4] = {i4.x, i4.y, i4.z, i4.w};
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
-                    const int64_t col = col0 + nt * 16 + ln;
+                    const int64_t col = col0 + (int64_t)nt * col_step + ln;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const uint32_t bit = 1u << (nt * 4 + q);
@@ -157,27 +233,19 @@ __device__ __forceinline__ void topk_epilogue(const floatx4 (&acc)[MW][NT], Topk
         }
         first = false;
         if (WG) __syncthreads(); else wave_sync();
-        const int li = lane & 31;
-        for (int r = hw0 + (lane >> 5); r < n_merge_rows; r += hw_step) {
-            const int cnt = t.ccnt[r];
+        const int li = lane & 15;
+        for (int r = q0 + (lane >> 4); r < n_merge_rows; r += q_step) {
+            const int cnt = min(t.ccnt[r], kCap);
             if (cnt == 0) continue;
-            float v;
-            int ix;
-            if (li < kTopK) {
-                v = t.lval[r * kTopK + li];
-                ix = t.lidx[r * kTopK + li];
-            } else if (li - kTopK < min(cnt, kCap)) {
-                v = t.cval[r * kCap + li - kTopK];
-                ix = t.cidx[r * kCap + li - kTopK];
-            } else {
-                v = -INFINITY;
-                ix = 0x7FFFFFFF;
-            }
-            bitonic_desc<32>(v, ix);
-            if (li < kTopK) {
-                t.lval[r * kTopK + li] = v;
-                t.lidx[r * kTopK + li] = ix;
-            }
+            const uint64_t kl = rank_key(t.lval[r * kTopK + li], t.lidx[r * kTopK + li]);
+            const uint64_t kc = li < cnt ? rank_key(t.cval[r * kCap + li], t.cidx[r * kCap + li]) : kEmptyKey;
+            uint64_t m = sort16<false>(kc, li);
+            m = m > kl ? m : kl;
+            m = merge16_desc(m, li);
+            const float v = key_value(m);
+            const int ix = key_id(m);
+            t.lval[r * kTopK + li] = v;
+            t.lidx[r * kTopK + li] = ix;
             if (li == kTopK - 1) {
                 t.thr[r] = v;
                 t.thri[r] = ix;
@@ -257,7 +325,10 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
     const int ri = lane / C::PIECES, pj = lane % C::PIECES;
     const int64_t row0 = t0 * 16;
     const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(W + row0 * D, (V - row0) * D * 2);
-    const int voff = ri * D * 2 + pj * 16;  // + q * ROWS_PER_LOAD * D * 2 + kc0 * 2 (scalar)
+    // The row goes into the lane offset (range-checked against the resource),
+    // the chunk's column offset into the scalar offset.
+    const int voff = ri * D * 2 + pj * 16;
+    const int qstride = C::ROWS_PER_LOAD * D * 2;
     unsigned char* hl = wl + C::R * C::ROWB;
     floatx4 acc[1][NTX];
 #pragma unroll
@@ -268,13 +339,13 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
 
     auto load = [&](u32x4 (&w)[C::LOADS], u32x4 (&hh)[C::ALOADS], int c, bool full) {
         const int kc0 = c * KC;
-        const int vo = (full || kc0 + pj * 8 < D) ? voff : kOffNone;
+        const bool in = full || kc0 + pj * 8 < D;
 #pragma unroll
         for (int q = 0; q < C::ALOADS; ++q)
-            hh[q] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, vo, (q * C::ROWS_PER_LOAD * D + kc0) * 2, 0);
+            hh[q] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, in ? voff + q * qstride : kOffNone, kc0 * 2, 0);
 #pragma unroll
         for (int q = 0; q < C::LOADS; ++q)
-            w[q] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, vo, (q * C::ROWS_PER_LOAD * D + kc0) * 2, kBufNT);
+            w[q] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, in ? voff + q * qstride : kOffNone, kc0 * 2, kBufNT);
     };
     auto stage = [&](const u32x4 (&w)[C::LOADS], const u32x4 (&hh)[C::ALOADS]) {
 #pragma unroll
@@ -285,7 +356,7 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
             *reinterpret_cast<u32x4*>(wl + (q * C::ROWS_PER_LOAD + ri) * C::ROWB + pj * 16) = w[q];
         wave_sync();
     };
-    auto compute = [&]() {
+    auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(hl + ln * C::ROWB + (32 * s + 8 * lg) * 2);
@@ -337,7 +408,7 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
         stage(w0, h0);
         compute();
     }
-    topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, t0 * 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 2);
+    topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, t0 * 16, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
 }
 
 template <int NT, int KS>
@@ -386,37 +457,68 @@ __global__ __launch_bounds__(256) void head_skinny2_kernel(const uint16_t* __res
     }
 }
 
-// --------------------------------------------------------------- wide GEMM
-template <int MW, int NT, int WM, int WN, int KS>
+// ------------------------------------------------ wide GEMM, LDS-staged W and h
+// head_wide_kernel (M > 16): a workgroup of 2 x 4 wavefronts (two per SIMD)
+// computes logits for an M-block of 32*MW rows of h against its contiguous,
+// balanced range of 16-row vocabulary tiles, in strips of 64*NT rows.
+// Wavefront (wm, wn) owns rows [16*MW*wm, 16*MW*(wm+1)) of the block and the
+// strip's tiles wn, wn+4, wn+8, ... (interleaved, so that a partial last strip
+// still spreads over all four SIMDs).  Per KC-wide chunk of the hidden
+// dimension all 512 threads read the h rows and the strip's W rows
+// row-contiguously with buffer loads DEPTH chunks ahead in registers, then
+// store one chunk into an LDS tile (row pitch KC*2+16 bytes, so the 16 rows
+// of a fragment read fall on distinct banks); with DBUF the tile is double
+// buffered and each chunk costs one barrier instead of two.  Fragments come
+// from LDS and the accumulators stay in registers.  A strip as wide as the
+// M-block makes re-reading h from L2 cost no more than streaming W.  The
+// top-16 epilogue's candidate buffers reuse the chunk tile's LDS.
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
 struct WideCfg {
-    static constexpr int MB = 16 * MW * WM;
+    static constexpr int THREADS = 128 * WN;          // 2 x WN wavefronts
     static constexpr int KC = 32 * KS;
-    static constexpr int LDS_ROW = KC + 8;  // bf16, 16-byte pad against bank conflicts
-    static constexpr int THREADS = 64 * WM * WN;
-    static constexpr int STRIP = 16 * NT * WN;
-    static constexpr int H_PIECES = MB * KC / 8;
-    static constexpr int H_PER_THREAD = (H_PIECES + THREADS - 1) / THREADS;
-    static constexpr size_t LDS_H = (size_t)MB * LDS_ROW * 2;
-    static constexpr size_t LDS_TOPK = (size_t)MB * (kTopK + kCap) * 8 + (size_t)MB * 12;
-    static constexpr size_t LDS = LDS_H + LDS_TOPK;
+    static constexpr int MB = 32 * MW;                // rows of h per workgroup
+    static constexpr int NB = 16 * WN * NT;           // W rows per strip
+    static constexpr int ROWB = KC * 2 + 16;
+    static constexpr int PIECES = KC / 8;             // 16-byte pieces per row and chunk
+    static constexpr int RPL = THREADS / PIECES;      // rows per workgroup-wide load
+    static constexpr int HLOADS = (MB + RPL - 1) / RPL;
+    static constexpr int WLOADS = NB / RPL;
+    static constexpr size_t TILE = (size_t)(MB + NB) * ROWB;
+    static constexpr size_t LDS_BUF = TILE * (DBUF ? 2 : 1);
+    static constexpr size_t LDS_LIST = (size_t)MB * kTopK * 8 + (size_t)MB * 12;
+    static constexpr size_t LDS = LDS_BUF + LDS_LIST;
+    static_assert((size_t)MB * kCap * 8 <= LDS_BUF, "candidate buffers must fit in the chunk tile");
+    static_assert(NB % RPL == 0 && WLOADS > 0, "whole W loads");
+    static_assert(LDS <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int MW, int NT, int WM, int WN, int KS>
-__global__ __launch_bounds__(64 * WM * WN) void head_wide_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t M, int D, int64_t V,
-    int n_strips, int S, int n_mb, float* __restrict__ part_val, int* __restrict__ part_idx) {
-    using C = WideCfg<MW, NT, WM, WN, KS>;
+// Calls f(std::integral_constant<int, j>) for j = k (0 <= k < N), so that
+// register arrays are indexed by a compile-time constant.
+template <int N, int J = 0, class F>
+__device__ __forceinline__ void with_slot(int k, F&& f) {
+    if constexpr (J < N) {
+        if (k == J) f(std::integral_constant<int, J>{});
+        else with_slot<N, J + 1>(k, f);
+    }
+}
+
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
+__global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2)))
+void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t M, int D,
+                      int64_t V, int64_t n_tiles, int S, int n_mb, float* __restrict__ part_val,
+                      int* __restrict__ part_idx) {
+    using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
+    constexpr int KC = C::KC;
     extern __shared__ __align__(16) unsigned char smem[];
-    uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
-    unsigned char* tp = smem + C::LDS_H;
+    unsigned char* lp = smem + C::LDS_BUF;
     TopkRows tk;
-    tk.lval = reinterpret_cast<float*>(tp);
-    tk.lidx = reinterpret_cast<int*>(tp + C::MB * kTopK * 4);
-    tk.cval = reinterpret_cast<float*>(tp + C::MB * kTopK * 8);
-    tk.cidx = reinterpret_cast<int*>(tp + C::MB * kTopK * 8 + C::MB * kCap * 4);
-    tk.thr = reinterpret_cast<float*>(tp + C::MB * (kTopK + kCap) * 8);
+    tk.lval = reinterpret_cast<float*>(lp);
+    tk.lidx = reinterpret_cast<int*>(lp + C::MB * kTopK * 4);
+    tk.thr = reinterpret_cast<float*>(lp + C::MB * kTopK * 8);
     tk.thri = reinterpret_cast<int*>(tk.thr + C::MB);
     tk.ccnt = tk.thri + C::MB;
+    tk.cval = reinterpret_cast<float*>(smem);  // aliases the chunk tile (epilogue only)
+    tk.cidx = reinterpret_cast<int*>(smem + C::MB * kCap * 4);
 
     // workgroup -> (M-block, slot): the M-blocks of one slot are dispatched
     // back to back on the same XCD so they share the slot's W rows in L2.
@@ -428,147 +530,138 @@ __global__ __launch_bounds__(64 * WM * WN) void head_wide_kernel(
     if (slot >= S) return;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
+    // wave-uniform (scalar) so that per-wavefront tile bounds become scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int ln = lane & 15, lg = lane >> 4;
     const int wm = wave / WN, wn = wave % WN;
+    const int ri = tid / C::PIECES, pj = tid % C::PIECES;  // workgroup-wide load mapping
     const int64_t m0 = (int64_t)mb * C::MB;
     const int rows_blk = (int)min<int64_t>(C::MB, M - m0);
     const int mw_act = max(0, min(MW, (rows_blk - wm * 16 * MW + 15) / 16));
     topk_init(tk, C::MB, tid, C::THREADS);
     __syncthreads();
 
-    const int s_begin = (int)((int64_t)slot * n_strips / S);
-    const int s_end = (int)((int64_t)(slot + 1) * n_strips / S);
-    const int n_chunks = (D + C::KC - 1) / C::KC;
-    const int n_full = D / C::KC;  // chunks without a ragged end
-    u32x4 hreg[C::H_PER_THREAD];
+    // Rows go into the lane offset (range-checked: rows past the block or the
+    // range read as zero), the chunk's column offset into the scalar offset.
+    const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(h + m0 * D, (int64_t)rows_blk * D * 2);
+    const int voff = ri * D * 2 + pj * 16;
+    const int qstride = C::RPL * D * 2;
+    const int64_t t_begin = (int64_t)slot * n_tiles / S, t_end = (int64_t)(slot + 1) * n_tiles / S;
+    const int n_full = D / KC;
+    const bool ktail = n_full * KC < D;
+    // Rows of h and W lie D*2 bytes apart, so the rows of one chunk fall on
+    // few memory channels; each workgroup starts its walk over the full
+    // chunks at a different chunk so that the grid spreads over all of them.
+    const int rot = n_full > 0 ? (int)(((int64_t)slot * 7 + mb * 3) % n_full) : 0;
 
-    // rows past the block repeat its last row (never read back); only a ragged
-    // last chunk masks k
-    auto load_h = [&](int c, bool full) {
-        const int kc0 = c * C::KC;
-#pragma unroll
-        for (int u = 0; u < C::H_PER_THREAD; ++u) {
-            const int p = min(tid + u * C::THREADS, C::H_PIECES - 1);
-            const int pr = p / (C::KC / 8), cp = p % (C::KC / 8);
-            const uint16_t* row = h + (m0 + min(pr, rows_blk - 1)) * D;
-            const int k = kc0 + cp * 8;
-            if (full) {
-                hreg[u] = ldg(row + k);
-            } else {
-                const u32x4 v = ldg(row + (k < D ? k : 0));
-                hreg[u] = k < D ? v : u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-    auto store_h = [&]() {
-#pragma unroll
-        for (int u = 0; u < C::H_PER_THREAD; ++u) {
-            const int p = tid + u * C::THREADS;
-            if (p < C::H_PIECES) {
-                const int pr = p / (C::KC / 8), cp = p % (C::KC / 8);
-                *reinterpret_cast<u32x4*>(hs + pr * C::LDS_ROW + cp * 8) = hreg[u];
-            }
-        }
-    };
-
-    for (int strip = s_begin; strip < s_end; ++strip) {
-        const int64_t col0 = (int64_t)strip * C::STRIP + wn * NT * 16;
-        const int nt_act = (int)max<int64_t>(0, min<int64_t>(NT, (V - col0 + 15) / 16));
-        const uint16_t* wrow[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            int64_t rr = col0 + nt * 16 + ln;
-            if (rr > V - 1) rr = V - 1;
-            wrow[nt] = W + rr * D;
-        }
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += C::NB / 16) {
+        // declared per strip: nothing in them lives across the epilogue
+        u32x4 hq[DEPTH][C::HLOADS], wq[DEPTH][C::WLOADS];
+        const int64_t col0 = t0 * 16;
+        const int tiles_here = (int)min<int64_t>(C::NB / 16, t_end - t0);
+        const int64_t rows_here = min<int64_t>((int64_t)tiles_here * 16, V - col0);
+        const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(W + col0 * D, rows_here * D * 2);
+        const int nt_act = max(0, min(NT, (tiles_here - wn + WN - 1) / WN));
+        const bool active = nt_act > 0 && mw_act > 0;
         floatx4 acc[MW][NT];
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        u32x4 wa[NT][KS], wb[NT][KS];
 
-        auto load_w = [&](u32x4 (&w)[NT][KS], int c, bool full) {
-            const int kc0 = c * C::KC;
+        auto load = [&](auto J, int c, bool full) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            const int kc0 = (full ? (c + rot) % n_full : c) * KC;
+            const bool in = full || kc0 + pj * 8 < D;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
+            for (int q = 0; q < C::HLOADS; ++q)
+                hq[j][q] = __builtin_amdgcn_raw_buffer_load_b128(hsrc, in ? voff + q * qstride : kOffNone, kc0 * 2, 0);
 #pragma unroll
-                for (int s = 0; s < KS; ++s) load_frag<KS>(w[nt][s], wrow[nt], kc0, s, lg, D, full, true);
+            for (int q = 0; q < C::WLOADS; ++q)
+                wq[j][q] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, in ? voff + q * qstride : kOffNone, kc0 * 2,
+                                                                 kBufNT);
         };
-        // A fragments of M-tile mt+1 are read from LDS while tile mt's MFMAs
-        // issue; the scheduling barrier keeps the compiler from hoisting all
-        // MW*KS fragments at once (register pressure).
-        auto compute = [&](const u32x4 (&w)[NT][KS]) {
-            const uint16_t* src = hs + (wm * 16 * MW + ln) * C::LDS_ROW + lg * 8;
-            u32x4 a_cur[KS], a_nxt[KS];
+        auto store = [&](auto J, int c) __attribute__((always_inline)) {
+            constexpr int j = decltype(J)::value;
+            unsigned char* tb = smem + (DBUF ? (size_t)(c & 1) * C::TILE : 0);
 #pragma unroll
-            for (int s = 0; s < KS; ++s) a_cur[s] = *reinterpret_cast<const u32x4*>(src + 32 * s);
+            for (int q = 0; q < C::HLOADS; ++q) {
+                const int row = q * C::RPL + ri;
+                if (C::MB % C::RPL == 0 || row < C::MB)
+                    *reinterpret_cast<u32x4*>(tb + row * C::ROWB + pj * 16) = hq[j][q];
+            }
+            unsigned char* wb = tb + C::MB * C::ROWB;
 #pragma unroll
-            for (int mt = 0; mt < MW; ++mt) {
-                if (mt < mw_act) {
-                    if (mt + 1 < MW && mt + 1 < mw_act) {
+            for (int q = 0; q < C::WLOADS; ++q)
+                *reinterpret_cast<u32x4*>(wb + (q * C::RPL + ri) * C::ROWB + pj * 16) = wq[j][q];
+        };
+        auto mfma_chunk = [&](int c, auto FULL) __attribute__((always_inline)) {
+            constexpr bool full = decltype(FULL)::value;
+            const unsigned char* tb = smem + (DBUF ? (size_t)(c & 1) * C::TILE : 0);
+            const unsigned char* ha = tb + (wm * 16 * MW + ln) * C::ROWB + lg * 16;
+            const unsigned char* wbp = tb + (C::MB + wn * 16 + ln) * C::ROWB + lg * 16;
 #pragma unroll
-                        for (int s = 0; s < KS; ++s)
-                            a_nxt[s] = *reinterpret_cast<const u32x4*>(src + (mt + 1) * 16 * C::LDS_ROW + 32 * s);
-                    }
+            for (int s = 0; s < KS; ++s) {
+                // all of the k-step's fragments first, then its MFMAs
+                u32x4 b[NT], a[MW];
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) {
-                        const bf16x8 av = __builtin_bit_cast(bf16x8, a_cur[s]);
+                for (int nt = 0; nt < NT; ++nt)
+                    if (full || nt < nt_act) b[nt] = *reinterpret_cast<const u32x4*>(wbp + nt * 16 * WN * C::ROWB + 64 * s);
 #pragma unroll
-                        for (int nt = 0; nt < NT; ++nt)
-                                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    av, __builtin_bit_cast(bf16x8, w[nt][s]), acc[mt][nt], 0, 0, 0);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int mt = 0; mt < MW; ++mt) a[mt] = *reinterpret_cast<const u32x4*>(ha + mt * 16 * C::ROWB + 64 * s);
 #pragma unroll
-                    for (int s = 0; s < KS; ++s) a_cur[s] = a_nxt[s];
-                }
+                for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        if (full || nt < nt_act)
+                            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, a[mt]), __builtin_bit_cast(bf16x8, b[nt]), acc[mt][nt],
+                                0, 0, 0);
             }
         };
-        // one chunk: h(c+1) to registers, W(c+1) in flight, MFMAs on chunk c,
-        // then h(c+1) into LDS (h loads are issued before the W loads so that
-        // waiting for them leaves the W loads outstanding)
-        // steady state over the full chunks: chunk c+1 is always loaded while
-        // chunk c computes, so the loads are unconditional; a ragged last
-        // chunk of the hidden dimension follows with masked loads
-        auto step = [&](const u32x4 (&cur)[NT][KS], u32x4 (&ahead)[NT][KS], int c) {
-            load_h(c + 1, true);
-            load_w(ahead, c + 1, true);
-            compute(cur);
-            __syncthreads();
-            store_h();
+        auto compute = [&](int c) __attribute__((always_inline)) {
+            if (nt_act == NT && mw_act > 0) mfma_chunk(c, std::true_type{});
+            else if (active) mfma_chunk(c, std::false_type{});
+        };
+        // Chunk c: multiply the staged chunk c, then stage chunk c+1 from its
+        // register slot and refill that slot with chunk c+1+DEPTH.
+        auto step = [&](auto J, int c, bool st, bool ld) __attribute__((always_inline)) {
+            compute(c);
+            if (!DBUF) __syncthreads();
+            if (st) store(J, c + 1);
+            if (ld) load(J, c + 1 + DEPTH, true);
             __syncthreads();
         };
         if (n_full > 0) {
-            load_h(0, true);
-            load_w(wa, 0, true);
-            store_h();
+#pragma unroll
+            for (int j = 0; j < DEPTH; ++j)
+                if (j < n_full) with_slot<DEPTH>(j, [&](auto J) __attribute__((always_inline)) { load(J, j, true); });
+            store(std::integral_constant<int, 0>{}, 0);
+            if (DEPTH < n_full) load(std::integral_constant<int, 0>{}, DEPTH, true);
             __syncthreads();
             int c = 0;
-            for (; c + 2 < n_full; c += 2) {
-                step(wa, wb, c);
-                step(wb, wa, c + 1);
+            for (; c + 2 * DEPTH <= n_full; c += DEPTH) {
+#pragma unroll
+                for (int j = 0; j < DEPTH; ++j)
+                    with_slot<DEPTH>((j + 1) % DEPTH,
+                                     [&](auto J) __attribute__((always_inline)) { step(J, c + j, true, true); });
             }
-            if (c + 1 < n_full) {
-                step(wa, wb, c);
-                compute(wb);
-            } else {
-                compute(wa);
-            }
+            for (; c < n_full; ++c)
+                with_slot<DEPTH>((c + 1) % DEPTH, [&](auto J) __attribute__((always_inline)) {
+                    step(J, c, c + 1 < n_full, c + 1 + DEPTH < n_full);
+                });
+            if (!DBUF) __syncthreads();
+        }
+        if (ktail) {
+            const auto J0 = std::integral_constant<int, 0>{};
+            load(J0, n_full, false);
+            store(J0, n_full);
+            __syncthreads();
+            compute(n_full);
             __syncthreads();
         }
-        if (n_full < n_chunks) {
-            load_h(n_full, false);
-            load_w(wa, n_full, false);
-            store_h();
-            __syncthreads();
-            compute(wa);
-            __syncthreads();
-        }
-        topk_epilogue<MW, NT, true>(acc, tk, wm * 16 * MW, m0 + wm * 16 * MW, M, col0, nt_act, V, mw_act,
-                                    rows_blk, wave * 2, WM * WN * 2);
+        topk_epilogue<MW, NT, true>(acc, tk, wm * 16 * MW, m0 + wm * 16 * MW, M, col0 + wn * 16, 16 * WN,
+                                    nt_act, V, mw_act, rows_blk, wave * 4, 8 * WN);
     }
 
     for (int e = tid; e < rows_blk * kTopK; e += C::THREADS) {
@@ -593,21 +686,27 @@ __global__ __launch_bounds__(64 * WM * WN) void head_wide_kernel(
 constexpr int kMaxLists = 1024;
 constexpr int kMergeSeg = 10;  // 16-byte pieces per lane per pass over D
 
-// Wavefront arg-max of (v, i) in ranks_before order; returns the winning lane.
-__device__ __forceinline__ int wave_argmax_lane(float& v, int& i) {
-    int who = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float v2 = __shfl_xor(v, off);
-        const int i2 = __shfl_xor(i, off);
-        const int w2 = __shfl_xor(who, off);
-        if (ranks_before(v2, i2, v, i) || (v2 == v && i2 == i && w2 < who)) {
-            v = v2;
-            i = i2;
-            who = w2;
-        }
-    }
-    return who;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t x) {
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, ROW_MASK, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(x >> 32), CTRL, ROW_MASK, 0xF, true);
+    const uint64_t y = ((uint64_t)hi << 32) | lo;
+    return y > x ? y : x;
+}
+
+// Wavefront maximum of a 64-bit key with DPP row shifts and row broadcasts;
+// every lane gets the result.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+    x = dpp_max_u64<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_max_u64<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_max_u64<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_max_u64<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_max_u64<0x142, 0xA>(x);  // row_bcast:15
+    x = dpp_max_u64<0x143, 0xC>(x);  // row_bcast:31
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, 63);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 // Pop the kRescore best entries of up to 64 sorted lists of length len held
@@ -619,23 +718,27 @@ __device__ __forceinline__ void extract_top(const float* lv, const int* li, int 
     float hv = lane < nlists ? lv[lane * len] : -INFINITY;
     int hi = lane < nlists ? li[lane * len] : 0x7FFFFFFF;
     for (int k = 0; k < kRescore; ++k) {
-        float bv = hv;
-        int bi = hi;
-        const int who = wave_argmax_lane(bv, bi);
-        if (lane == 0) {
-            ov[k] = bv;
-            oi[k] = bi;
-        }
-        if (lane == who) {
-            ++pos;
-            hv = pos < len ? lv[lane * len + pos] : -INFINITY;
-            hi = pos < len ? li[lane * len + pos] : 0x7FFFFFFF;
+        const uint64_t mine = rank_key(hv, hi);
+        const uint64_t best = wave_max_u64(mine);
+        // The winner is unique (distinct ids) unless only sentinels are left;
+        // then every lane ties and the first writes a sentinel.  Only lanes
+        // that own a list advance, and never past its end.
+        if (mine == best) {
+            if (lane == __builtin_amdgcn_readfirstlane(lane)) {
+                ov[k] = hv;
+                oi[k] = hi;
+            }
+            if (lane < nlists && pos < len) {
+                ++pos;
+                hv = pos < len ? lv[lane * len + pos] : -INFINITY;
+                hi = pos < len ? li[lane * len + pos] : 0x7FFFFFFF;
+            }
         }
     }
 }
 
 __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int D, int S,
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int D, int64_t V, int S,
     const float* __restrict__ part_val, const int* __restrict__ part_idx,
     float* __restrict__ top_val, int32_t* __restrict__ top_idx) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -652,9 +755,25 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
     const int wave = tid >> 6, lane = tid & 63;
     const float4* pv4 = reinterpret_cast<const float4*>(part_val + m * S * kTopK);
     const int4* pi4 = reinterpret_cast<const int4*>(part_idx + m * S * kTopK);
-    for (int e = tid; e < S * kTopK / 4; e += kMergeThreads) {
-        reinterpret_cast<float4*>(lv)[e] = pv4[e];
-        reinterpret_cast<int4*>(li)[e] = pi4[e];
+    {  // all loads of the copy are issued before any store
+        constexpr int kIters = (kMaxLists * kTopK / 4 + kMergeThreads - 1) / kMergeThreads;
+        const int n4 = S * kTopK / 4;
+        float4 cv[kIters];
+        int4 ci[kIters];
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = min(tid + it * kMergeThreads, n4 - 1);  // unconditional loads
+            cv[it] = pv4[e];
+            ci[it] = pi4[e];
+        }
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = tid + it * kMergeThreads;
+            if (e < n4) {
+                reinterpret_cast<float4*>(lv)[e] = cv[it];
+                reinterpret_cast<int4*>(li)[e] = ci[it];
+            }
+        }
     }
     __syncthreads();
     const int ng = (S + 63) / 64;
@@ -664,7 +783,11 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
     if (wave == 0) extract_top(&gv[0][0], &gi[0][0], kRescore, ng, sel_v, sel_i);
     __syncthreads();
     int ns = 0;
-    for (int c = 0; c < kRescore; ++c) ns += (sel_i[c] != 0x7FFFFFFF) ? 1 : 0;
+    // real entries precede the sentinels; an id outside [0, V) (none is
+    // expected) ends the list rather than being dereferenced
+    for (int c = 0; c < kRescore; ++c) {
+        if (ns == c && sel_i[c] >= 0 && sel_i[c] < V) ++ns;
+    }
 
     // exact re-scoring, two candidates per wavefront
     const uint16_t* hr = h + m * D;
@@ -722,64 +845,63 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
 // ------------------------------------------------------------------ host
 namespace {
 
-enum HeadVariant { kSkinny = 0, kWide64 = 1, kWide128 = 2, kWide256 = 3 };
+enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2 };
 
 struct HeadPlan {
     HeadVariant variant;
-    int mb_rows;    // rows per M-block (wide) / 16 (skinny)
-    int strip;      // vocabulary rows per strip (wide)
+    int mb_rows;    // rows per M-block
     int S;          // partial lists per row (= workgroups per M-block)
     int n_mb;
-    int n_strips;
+    int64_t n_tiles;
 };
 
-using Wide64 = WideCfg<4, 2, 1, 4, 4>;
-using Wide128 = WideCfg<8, 2, 1, 4, 4>;
-using Wide256 = WideCfg<8, 2, 2, 4, 4>;
+// One instantiation of head_wide_kernel with its launch.
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
+struct WideVariant {
+    using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
+    static const void* fn() { return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN>); }
+    static void set_attr() {
+        (void)hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+    }
+    static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
+                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
+        const int grid = (S + 7) / 8 * 8 * n_mb;
+        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN>), dim3(grid), dim3(Cfg::THREADS), Cfg::LDS, stream, h,
+                           W, M, D, V, n_tiles, S, n_mb, pv, pi);
+    }
+};
+
 constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWG = 512;  // 2 workgroups (8 wavefronts) per CU
+// Measured on MI355X (V = 151936, D = 5120) among the register-feasible
+// instantiations: 8 wavefronts with 64x32 / 112x32 wavefront tiles.
+using Wide128 = WideVariant<4, 2, 2, 4, true, 4>;  // M-blocks of 128 rows
+using Wide224 = WideVariant<7, 2, 2, 2, true, 4>;  // M-blocks of 224 rows
+constexpr int kCUs = 256;
 
 HeadPlan head_plan(int64_t M, int64_t V) {
     HeadPlan p{};
+    p.n_tiles = (V + 15) / 16;
     if (M <= 16) {
         p.variant = kSkinny;
         p.mb_rows = 16;
         p.n_mb = 1;
-        const int64_t n_tiles = (V + 15) / 16;
-        const int64_t want = (n_tiles + 3) / 4;  // at least one tile per wavefront
+        const int64_t want = (p.n_tiles + 3) / 4;  // at least one tile per wavefront
         p.S = (int)std::min<int64_t>(kSkinnyWG, want);
-        p.strip = 16;
-        p.n_strips = (int)n_tiles;
         return p;
     }
-    int slots;
-    if (M <= 64) {
-        p.variant = kWide64;
-        p.mb_rows = Wide64::MB;
-        p.strip = Wide64::STRIP;
-        slots = 512;
-    } else if (M <= 128) {
+    if (M <= 128) {
         p.variant = kWide128;
-        p.mb_rows = Wide128::MB;
-        p.strip = Wide128::STRIP;
-        slots = 512;
+        p.mb_rows = Wide128::Cfg::MB;
     } else {
-        p.variant = kWide256;
-        p.mb_rows = Wide256::MB;
-        p.strip = Wide256::STRIP;
-        slots = 256;  // one 8-wavefront workgroup per CU
+        p.variant = kWide224;  // M-blocks of 224 rows
+        p.mb_rows = Wide224::Cfg::MB;
     }
     p.n_mb = (int)((M + p.mb_rows - 1) / p.mb_rows);
-    p.n_strips = (int)((V + p.strip - 1) / p.strip);
-    int s = std::max(1, slots / p.n_mb);
-    s = std::min(s, p.n_strips);
-    p.S = std::min((s + 7) / 8 * 8, kMaxLists);  // whole XCD rounds of slots
+    // one workgroup per CU (the chunk tile takes most of the LDS)
+    int s = std::max(1, kCUs / p.n_mb);
+    s = (int)std::min<int64_t>(s, p.n_tiles);  // at least one tile each
+    p.S = std::min(s, kMaxLists);
     return p;
-}
-
-template <typename Cfg, typename K>
-void set_lds(K kernel) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)Cfg::LDS);
 }
 
 std::once_flag g_head_attr_once;
@@ -794,38 +916,30 @@ size_t head_workspace_bytes(int64_t M, int64_t V) {
 int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
                      float* top_val, int32_t* top_idx, void* ws, hipStream_t stream) {
     std::call_once(g_head_attr_once, []() {
-        set_lds<Wide64>(&head_wide_kernel<4, 2, 1, 4, 4>);
-        set_lds<Wide128>(&head_wide_kernel<8, 2, 1, 4, 4>);
-        set_lds<Wide256>(&head_wide_kernel<8, 2, 2, 4, 4>);
+        Wide128::set_attr();
+        Wide224::set_attr();
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLists * kTopK * 8);
     });
     const HeadPlan p = head_plan(M, V);
     float* pv = reinterpret_cast<float*>(ws);
     int* pi = reinterpret_cast<int*>(pv + (size_t)M * p.S * kTopK);
-    const dim3 grid(p.S * p.n_mb);
     switch (p.variant) {
         case kSkinny:
             hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS>), dim3(p.S), dim3(256), 0, stream, h, W, M,
-                               D, V, (int64_t)p.n_strips, pv, pi);
-            break;
-        case kWide64:
-            hipLaunchKernelGGL((head_wide_kernel<4, 2, 1, 4, 4>), grid, dim3(Wide64::THREADS), Wide64::LDS, stream,
-                               h, W, M, D, V, p.n_strips, p.S, p.n_mb, pv, pi);
+                               D, V, p.n_tiles, pv, pi);
             break;
         case kWide128:
-            hipLaunchKernelGGL((head_wide_kernel<8, 2, 1, 4, 4>), grid, dim3(Wide128::THREADS), Wide128::LDS, stream,
-                               h, W, M, D, V, p.n_strips, p.S, p.n_mb, pv, pi);
+            Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
         default:
-            hipLaunchKernelGGL((head_wide_kernel<8, 2, 2, 4, 4>), grid, dim3(Wide256::THREADS), Wide256::LDS, stream,
-                               h, W, M, D, V, p.n_strips, p.S, p.n_mb, pv, pi);
+            Wide224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
     }
     int st = launch_status();
     if (st != DFLASH_OK) return st;
     const size_t lds = (size_t)p.S * kTopK * 8;
-    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), lds, stream, h, W, D, p.S, pv,
+    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), lds, stream, h, W, D, V, p.S, pv,
                        pi, top_val, top_idx);
     return launch_status();
 }

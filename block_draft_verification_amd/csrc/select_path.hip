@@ -10,111 +10,100 @@
 // [V][r]; max-sum DP  delta_{p+1}[j] = val[p+1][j] + max_i(delta_p[i] + pair_p[i][j]),
 // lowest i on ties, path ending at the lowest maximiser and read back.
 //
-// One workgroup per request of up to four groups of 256 threads.  Group g owns
-// the pair tiles p = g, g+groups, ...: it gathers the 16 left rows and 16 right rows
-// of the tables into LDS (transposed, k-major, pitch 17, so the 16 lanes of a
-// tile row read consecutive words), then thread (i, j) sums over k = 0..r-1 in order in
-// float64 (each float32 product is exact in float64, so the fused multiply-add
-// rounds exactly like an add of the exact product).  All tiles stay in LDS;
-// sixteen lanes then run the DP over the P positions with the back-pointers in
-// LDS, and one lane reads the path back.
+// Kernel 1 (select_pairs_kernel), one 256-thread workgroup per (request,
+// adjacent position pair): gathers the 16 left rows and the 16 right rows of
+// the tables into LDS (vectorised loads, all issued first; k-major with a
+// pitch of 17 floats so that both the transposing stores and the reads are
+// free of bank conflicts), then thread (i, j) sums over k = 0..r-1 in order in
+// float64 (each float32 product is exact in float64, so the fused
+// multiply-add rounds exactly like an add of the exact product) and writes the
+// 16x16 tile to the workspace.
+// Kernel 2 (select_dp_kernel), one wavefront per request: sixteen lanes run
+// the DP over the P positions with the back-pointers in LDS; one lane reads
+// the path back.  All DP arithmetic is float64.
 
 #include "common.hpp"
 
 namespace dflash {
 
-constexpr int kSelMaxGroups = 4;
-constexpr int kSelThreads = 256 * kSelMaxGroups;
 constexpr int kMaxP = 15;
-constexpr int kMaxVec = 4;  // float4s per thread per table: 16 rows x r <= 256 floats / 256 threads
+constexpr int kMaxVec = 4;         // float4s per thread per table: 16 rows x r <= 256 floats / 256 threads
 constexpr int kPitch = kTopK + 1;  // floats per k in the staged tables
 
-__global__ __launch_bounds__(kSelThreads) void select_path_kernel(
-    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx,
-    const float* __restrict__ feat_l, const float* __restrict__ feat_r, int P, int64_t V, int r,
-    int32_t* __restrict__ path_rank, int32_t* __restrict__ path_tok,
-    float* __restrict__ path_score) {
-    extern __shared__ float stage[];  // [groups][2][r][kPitch], groups = blockDim.x / 256
-    __shared__ double pair[kMaxP - 1][kTopK][kTopK];
+__global__ __launch_bounds__(256) void select_pairs_kernel(const int32_t* __restrict__ top_idx,
+                                                           const float* __restrict__ feat_l,
+                                                           const float* __restrict__ feat_r, int P, int64_t V,
+                                                           int r, double* __restrict__ pairs) {
+    __shared__ float sl[256 * kPitch];
+    __shared__ float sr[256 * kPitch];
+    __shared__ int il_s[kTopK], ir_s[kTopK];
+    const int p = blockIdx.x;   // pair (p, p+1)
+    const int b = blockIdx.y;   // request
+    const int lt = threadIdx.x;
+    if (lt < kTopK) {
+        il_s[lt] = top_idx[((int64_t)b * P + p) * kTopK + lt];
+        ir_s[lt] = top_idx[((int64_t)b * P + p + 1) * kTopK + lt];
+    }
+    __syncthreads();
+    const int r4 = r >> 2;
+    floatx4 ql[kMaxVec], qr[kMaxVec];
+#pragma unroll
+    for (int u = 0; u < kMaxVec; ++u) {
+        const int e = lt + 256 * u;
+        ql[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        qr[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (e < kTopK * r4) {
+            const int row = e / r4, k4 = e - row * r4;
+            const int il = il_s[row], ir = ir_s[row];
+            // ids outside [0, V) contribute a zero feature row
+            if (il >= 0 && il < V) ql[u] = *reinterpret_cast<const floatx4*>(feat_l + (int64_t)il * r + 4 * k4);
+            if (ir >= 0 && ir < V) qr[u] = *reinterpret_cast<const floatx4*>(feat_r + (int64_t)ir * r + 4 * k4);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kMaxVec; ++u) {
+        const int e = lt + 256 * u;
+        if (e < kTopK * r4) {
+            const int row = e / r4, k = 4 * (e - row * r4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                sl[(k + q) * kPitch + row] = ql[u][q];
+                sr[(k + q) * kPitch + row] = qr[u][q];
+            }
+        }
+    }
+    __syncthreads();
+    const int i = lt >> 4, j = lt & 15;
+    double acc = 0.0;
+#pragma unroll 16
+    for (int k = 0; k < r; ++k) acc = fma((double)sl[k * kPitch + i], (double)sr[k * kPitch + j], acc);
+    pairs[(((int64_t)b * (P - 1) + p) * kTopK + i) * kTopK + j] = acc;
+}
+
+__global__ __launch_bounds__(64) void select_dp_kernel(const float* __restrict__ top_val,
+                                                       const int32_t* __restrict__ top_idx,
+                                                       const double* __restrict__ pairs, int P,
+                                                       int32_t* __restrict__ path_rank,
+                                                       int32_t* __restrict__ path_tok,
+                                                       float* __restrict__ path_score) {
     __shared__ double val_s[kMaxP][kTopK];
-    __shared__ int idx_s[kMaxP][kTopK];
     __shared__ unsigned char psi[kMaxP][kTopK];
     __shared__ double delta[kTopK];
-
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int nthreads = blockDim.x;
-    const int groups = nthreads >> 8;
-    for (int e = tid; e < P * kTopK; e += nthreads) {
-        val_s[e / kTopK][e % kTopK] = (double)top_val[(int64_t)b * P * kTopK + e];
-        idx_s[e / kTopK][e % kTopK] = top_idx[(int64_t)b * P * kTopK + e];
-    }
+    for (int e = tid; e < P * kTopK; e += 64) val_s[e / kTopK][e % kTopK] = (double)top_val[(int64_t)b * P * kTopK + e];
+    if (tid < kTopK) delta[tid] = (double)top_val[(int64_t)b * P * kTopK + tid];
     __syncthreads();
-
-    const int g = tid >> 8;
-    const int lt = tid & 255;
-    float* sl = stage + (size_t)g * 2 * r * kPitch;
-    float* sr = sl + (size_t)r * kPitch;
-    const int rounds = (P - 1 + groups - 1) / groups;
-    for (int round = 0; round < rounds; ++round) {
-        const int p = round * groups + g;
-        const bool active = p < P - 1;
-        if (active) {
-            // 16 rows x r floats per table = 4*r float4s; thread lt takes float4s
-            // lt, lt+256, ... (at most kMaxVec of them), all loads issued first.
-            // LDS layout is k-major with a row pitch of 17 floats, so both the
-            // transposing stores and the (i, j) reads are free of bank conflicts.
-            const int r4 = r >> 2;
-            floatx4 ql[kMaxVec], qr[kMaxVec];
-#pragma unroll
-            for (int u = 0; u < kMaxVec; ++u) {
-                const int e = lt + 256 * u;
-                ql[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-                qr[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-                if (e < kTopK * r4) {
-                    const int row = e / r4, k4 = e - row * r4;
-                    const int il = idx_s[p][row], ir = idx_s[p + 1][row];
-                    // ids outside [0, V) contribute a zero feature row
-                    if (il >= 0 && il < V) ql[u] = *reinterpret_cast<const floatx4*>(feat_l + (int64_t)il * r + 4 * k4);
-                    if (ir >= 0 && ir < V) qr[u] = *reinterpret_cast<const floatx4*>(feat_r + (int64_t)ir * r + 4 * k4);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kMaxVec; ++u) {
-                const int e = lt + 256 * u;
-                if (e < kTopK * r4) {
-                    const int row = e / r4, k = 4 * (e - row * r4);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        sl[(k + q) * kPitch + row] = ql[u][q];
-                        sr[(k + q) * kPitch + row] = qr[u][q];
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        if (active) {
-            const int i = lt >> 4, j = lt & 15;
-            double acc = 0.0;
-#pragma unroll 16
-            for (int k = 0; k < r; ++k)
-                acc = fma((double)sl[k * kPitch + i], (double)sr[k * kPitch + j], acc);
-            pair[p][i][j] = acc;
-        }
-        __syncthreads();
-    }
-
-    // max-sum DP over positions (16 lanes), back-pointers in LDS
-    if (tid < kTopK) delta[tid] = val_s[0][tid];
-    __syncthreads();
+    const double* pb = pairs + (int64_t)b * (P - 1) * kTopK * kTopK;
     for (int p = 0; p + 1 < P; ++p) {
         double nd = 0.0;
         if (tid < kTopK) {
             const int j = tid;
-            double best = delta[0] + pair[p][0][j];
+            const double* pp = pb + (int64_t)p * kTopK * kTopK;
+            double best = delta[0] + pp[j];
             int bi = 0;
             for (int i = 1; i < kTopK; ++i) {
-                const double c = delta[i] + pair[p][i][j];
+                const double c = delta[i] + pp[i * kTopK + j];
                 if (c > best) {
                     best = c;
                     bi = i;
@@ -138,29 +127,27 @@ __global__ __launch_bounds__(kSelThreads) void select_path_kernel(
         int cur = end;
         for (int p = P - 1; p >= 0; --p) {
             path_rank[(int64_t)b * P + p] = cur;
-            path_tok[(int64_t)b * P + p] = idx_s[p][cur];
+            path_tok[(int64_t)b * P + p] = top_idx[((int64_t)b * P + p) * kTopK + cur];
             if (p > 0) cur = psi[p][cur];
         }
         path_score[b] = (float)best;
     }
 }
 
+size_t select_workspace_bytes(int B, int P) { return (size_t)B * (P > 1 ? P - 1 : 1) * kTopK * kTopK * 8; }
+
 int launch_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
                        const float* feat_r, int B, int P, int64_t V, int r, int32_t* path_rank,
-                       int32_t* path_tok, float* path_score, hipStream_t stream) {
-    // as many concurrent tile groups as the tiles and 96 KiB of staging allow
-    int groups = kSelMaxGroups;
-    while (groups > 1 && (size_t)groups * 2 * r * kPitch * sizeof(float) > 96 * 1024) groups >>= 1;
-    while (groups > 1 && groups / 2 >= P - 1) groups >>= 1;
-    const size_t shmem = (size_t)groups * 2 * r * kPitch * sizeof(float);
-    static bool attr_done = false;
-    if (!attr_done) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&select_path_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
-        attr_done = true;
+                       int32_t* path_tok, float* path_score, void* ws, hipStream_t stream) {
+    double* pairs = reinterpret_cast<double*>(ws);
+    if (P > 1) {
+        hipLaunchKernelGGL(select_pairs_kernel, dim3(P - 1, B), dim3(256), 0, stream, top_idx, feat_l, feat_r, P, V,
+                           r, pairs);
+        const int st = launch_status();
+        if (st != DFLASH_OK) return st;
     }
-    hipLaunchKernelGGL(select_path_kernel, dim3(B), dim3(256 * groups), shmem, stream, top_val, top_idx,
-                       feat_l, feat_r, P, V, r, path_rank, path_tok, path_score);
+    hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(64), 0, stream, top_val, top_idx, pairs, P, path_rank,
+                       path_tok, path_score);
     return launch_status();
 }
 

@@ -122,19 +122,20 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
  * lowest i on ties, path ending at the lowest maximiser of delta_{P-1}.
  * Pair sums run over k = 0..r-1 in order and the DP in float64.
  *   top_val    f32 [B][P][K]   candidate draft logits (from dflash_head_topk)
- *   top_idx    i32 [B][P][K]   candidate vocab ids, each in [0, V)
+ *   top_idx    i32 [B][P][K]   candidate vocab ids; ids outside [0, V) score 0
  *   feat_l/r   f32 [V][r]      16-byte aligned
  *   path_rank  i32 [B][P]      chosen candidate rank per position
  *   path_tok   i32 [B][P]      chosen vocab id per position (the draft tokens)
  *   path_score f32 [B]         float32 of the path's float64 score
  * Requires B >= 1, 1 <= P <= 15, V >= 1, 4 <= r <= 256, r % 4 == 0;
- * K == 16 (else UNSUPPORTED).
+ * K == 16 (else UNSUPPORTED).  Workspace: the pair tiles (B*(P-1)*16*16
+ * doubles), see the workspace convention above.
  */
 int dflash_select_path(const float* top_val, const int32_t* top_idx,
                        const float* feat_l, const float* feat_r,
                        int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
                        int32_t* path_rank, int32_t* path_tok, float* path_score,
-                       void* stream);
+                       void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * Greedy verification.

@@ -99,15 +99,21 @@ def test_head_validation_and_workspace():
 @needs_lib
 def test_select_validation():
     f = dfl.lib().dflash_select_path
-    args = lambda B, P, K, V, r, out0=A[4]: (A[0], A[1], A[2], A[3], B, P, K, V, r, out0, A[5], A[6], NULL)
+    n = ctypes.c_size_t(0)
+    args = lambda B, P, K, V, r, out0=A[4], ws=NULL: (A[0], A[1], A[2], A[3], B, P, K, V, r, out0, A[5], A[6],
+                                                      ws, ctypes.byref(n), NULL)
     assert f(*args(1, 7, 8, 4096, 32)) == UNSUPPORTED
     assert f(*args(1, 16, 16, 4096, 32)) == INVALID
     assert f(*args(1, 0, 16, 4096, 32)) == INVALID
     assert f(*args(1, 7, 16, 4096, 30)) == INVALID
     assert f(*args(1, 7, 16, 4096, 512)) == INVALID
     assert f(*args(1, 7, 16, 4096, 32, out0=A[0])) == INVALID
+    assert f(*args(4, 7, 16, 4096, 32)) == OK and n.value == 4 * 6 * 16 * 16 * 8
+    n.value = 100
+    assert f(*args(4, 7, 16, 4096, 32, ws=A[7])) == WORKSPACE
     if not torch.cuda.is_available():
-        assert f(*args(2, 7, 16, 4096, 192)) == DEVICE
+        n.value = 1 << 20
+        assert f(*args(2, 7, 16, 4096, 192, ws=A[7])) == DEVICE
 
 
 @needs_lib
