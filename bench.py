@@ -48,7 +48,22 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--max-sets", type=int, default=64)
+    ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
+                    help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
     return ap.parse_args()
+
+
+def copy_probe(gib):
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 copies of {n} bytes")
 
 
 class CycleRunner:
@@ -177,7 +192,7 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
     ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
-    while total + t1 <= seconds and n < 5:
+    while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
         run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
         total += time.perf_counter() - t0
@@ -199,6 +214,9 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
 
 def main():
     args = parse()
+    if args.copy_probe is not None:
+        copy_probe(args.copy_probe)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: this library has no multi-GPU path "
