@@ -105,7 +105,7 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
                      float* top_val, int32_t* top_idx, void* workspace, size_t* workspace_bytes,
                      void* stream) {
     if (!h || !W || !top_val || !top_idx) return DFLASH_ERR_INVALID;
-    if (M < 1 || D < 8 || D % 8 != 0 || V < 1) return DFLASH_ERR_INVALID;
+    if (M < 1 || D < 8 || D % 8 != 0 || D > 65536 || V < 1) return DFLASH_ERR_INVALID;
     if (K != 16) return DFLASH_ERR_UNSUPPORTED;
     if (V < K || V >= ((int64_t)1 << 31) || M > ((int64_t)1 << 24)) return DFLASH_ERR_INVALID;
     if (!aligned16(h) || !aligned16(W) || !aligned4(top_val) || !aligned4(top_idx)) return DFLASH_ERR_INVALID;

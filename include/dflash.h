@@ -101,7 +101,8 @@ int dflash_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y,
  *   W        bf16 [V][D]     LM-head rows (vocab entry v is row v)
  *   top_val  f32  [M][K]     output values, descending
  *   top_idx  i32  [M][K]     output vocab ids
- * Requires M >= 1, D >= 8, D % 8 == 0, V >= K; K == 16 (else UNSUPPORTED).
+ * Requires M >= 1, 8 <= D <= 65536, D % 8 == 0, K <= V < 2^31, M <= 2^24;
+ * K == 16 (else UNSUPPORTED).
  * Workspace: partial candidate lists, see the workspace convention above.
  */
 int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,

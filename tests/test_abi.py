@@ -85,6 +85,8 @@ def test_head_validation_and_workspace():
     assert ws_query(f, A[0], A[1], 7, 5120, 15, 16, A[2], A[3])[0] == INVALID     # V < K
     assert ws_query(f, A[0], A[1], 0, 5120, 4096, 16, A[2], A[3])[0] == INVALID
     assert ws_query(f, A[0], A[1], 7, 5121, 4096, 16, A[2], A[3])[0] == INVALID
+    assert ws_query(f, A[0], A[1], 7, 65544, 4096, 16, A[2], A[3])[0] == INVALID   # D > 65536
+    assert ws_query(f, A[0], A[1], 7, 65536, 4096, 16, A[2], A[3])[0] == OK
     assert ws_query(f, NULL, A[1], 7, 256, 4096, 16, A[2], A[3])[0] == INVALID
     small = ctypes.c_size_t(need - 1)
     assert f(A[0], A[1], 7, 5120, 151936, 16, A[2], A[3], A[4], ctypes.byref(small), NULL) == WORKSPACE
