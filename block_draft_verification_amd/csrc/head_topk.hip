@@ -47,6 +47,16 @@
 
 namespace dflash {
 
+// LDS row padding of the staged tiles.  A fragment read (lane l: row l % 16,
+// 16 bytes at column granule l / 16) is serviced by gfx950 for lanes 0-7 and
+// 16-23 together (then 8-15 with 24-31, ...), i.e. rows 0..7 at two adjacent
+// 16-byte granules.  With a pitch of p granules those fall on bank groups
+// {p r, p r + 1 : r < 8} mod 16, all distinct iff p = 2 (mod 4); the data part
+// (KC*2 bytes, KC a multiple of 32) is 0 (mod 4) granules, so 2 granules of
+// padding.  (Measured: 16 bytes of padding doubles the cost of every fragment
+// read; 32 bytes reaches the contiguous rate.)
+constexpr int kPitchPad = 32;
+
 constexpr int kCap = 16;        // candidate slots per row between merges
 static_assert(kCap == 16, "one buffered candidate per lane of a 16-lane row");
 constexpr int kRescore = 20;    // float32 candidates re-scored exactly per row
@@ -124,21 +134,24 @@ __device__ __forceinline__ float key_value(uint64_t k) {
 __device__ __forceinline__ int key_id(uint64_t k) { return 0x7FFFFFFF - (int)(uint32_t)k; }
 constexpr uint64_t kEmptyKey = 0x007FFFFF00000000ull;  // rank_key(-inf, 0x7FFFFFFF)
 
-// A 64-bit value from another lane of the same 16-lane row (DPP control CTRL).
+// A 64-bit value from another lane of the same 16-lane row (DPP control CTRL;
+// every source lane is inside the row, so no bound control is involved).
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, true);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, true);
     return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t xor4_u64(uint64_t x) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, 4);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), 4);
-    return ((uint64_t)hi << 32) | lo;
+// Lane ^ 4 within a row: row_shl:4 brings lane i+4, row_shr:4 lane i-4.
+__device__ __forceinline__ uint64_t xor4_u64(uint64_t x, int li) {
+    const uint64_t up = dpp_u64<0x104>(x);
+    const uint64_t dn = dpp_u64<0x114>(x);
+    return (li & 4) ? dn : up;
 }
 // Compare-exchange with the partner's key p: keep the larger key if keep_max.
 __device__ __forceinline__ uint64_t cx(uint64_t k, uint64_t p, bool keep_max) {
-    return ((p > k) == keep_max) ? p : k;
+    const bool take = (p > k) == keep_max;
+    return take ? p : k;
 }
 // DPP controls: quad_perm [1,0,3,2] / [2,3,0,1] / [3,2,1,0] (lane ^ 1, ^ 2, ^ 3),
 // row_half_mirror (^ 7), row_mirror (^ 15), row_ror:8 (^ 8).
@@ -146,7 +159,7 @@ constexpr int kDppX1 = 0xB1, kDppX2 = 0x4E, kDppX3 = 0x1B, kDppX7 = 0x141, kDppX
 
 // Bitonic sort of one key per lane over each 16-lane row, descending if DESC.
 // Every merge stage starts with the mirrored comparison (lane ^ (2s - 1)) so
-// all blocks sort in the same direction; only lane ^ 4 needs a permute.
+// all blocks sort in the same direction; lane ^ 4 takes two row shifts.
 template <bool DESC>
 __device__ __forceinline__ uint64_t sort16(uint64_t k, int li) {
     k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
@@ -156,7 +169,7 @@ __device__ __forceinline__ uint64_t sort16(uint64_t k, int li) {
     k = cx(k, dpp_u64<kDppX2>(k), ((li & 2) == 0) == DESC);
     k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
     k = cx(k, dpp_u64<kDppX15>(k), ((li & 8) == 0) == DESC);
-    k = cx(k, xor4_u64(k), ((li & 4) == 0) == DESC);
+    k = cx(k, xor4_u64(k, li), ((li & 4) == 0) == DESC);
     k = cx(k, dpp_u64<kDppX2>(k), ((li & 2) == 0) == DESC);
     k = cx(k, dpp_u64<kDppX1>(k), ((li & 1) == 0) == DESC);
     return k;
@@ -164,7 +177,7 @@ __device__ __forceinline__ uint64_t sort16(uint64_t k, int li) {
 // Sort a bitonic sequence of 16 keys (one per lane of a row) descending.
 __device__ __forceinline__ uint64_t merge16_desc(uint64_t k, int li) {
     k = cx(k, dpp_u64<kDppX8>(k), (li & 8) == 0);
-    k = cx(k, xor4_u64(k), (li & 4) == 0);
+    k = cx(k, xor4_u64(k, li), (li & 4) == 0);
     k = cx(k, dpp_u64<kDppX2>(k), (li & 2) == 0);
     k = cx(k, dpp_u64<kDppX1>(k), (li & 1) == 0);
     return k;
@@ -288,14 +301,14 @@ __device__ __forceinline__ void load_frag(u32x4& out, const uint16_t* row, int k
 // so that its HBM reads are row-contiguous: per chunk the wavefront's 16*NT
 // rows x KC columns are read as 512/KC rows per load instruction (64 lanes x
 // 16 contiguous bytes), written to the wavefront's private LDS tile, and read
-// back in the MFMA operand layout (row pitch KC*2+16 bytes, so the 16 rows of a
-// fragment read fall on disjoint bank groups).  Contiguous runs of 2*KC bytes
-// per row instead of 64-byte pieces keep HBM pages open.
+// back in the MFMA operand layout (row pitch KC*2 + kPitchPad bytes).
+// Contiguous runs of 2*KC bytes per row instead of 64-byte pieces keep HBM
+// pages open.
 template <int NT, int KS>
 struct Skinny2Cfg {
     static constexpr int KC = 32 * KS;
     static constexpr int R = 16 * NT;                 // W rows per wavefront tile
-    static constexpr int ROWB = KC * 2 + 16;          // LDS bytes per staged row
+    static constexpr int ROWB = KC * 2 + kPitchPad;   // LDS bytes per staged row
     static constexpr int PIECES = KC / 8;             // 16-byte pieces per row
     static constexpr int ROWS_PER_LOAD = 64 / PIECES;
     static constexpr int LOADS = R / ROWS_PER_LOAD;   // W load instructions per chunk
@@ -466,8 +479,8 @@ __global__ __launch_bounds__(256) void head_skinny2_kernel(const uint16_t* __res
 // still spreads over all four SIMDs).  Per KC-wide chunk of the hidden
 // dimension all 512 threads read the h rows and the strip's W rows
 // row-contiguously with buffer loads DEPTH chunks ahead in registers, then
-// store one chunk into an LDS tile (row pitch KC*2+16 bytes, so the 16 rows
-// of a fragment read fall on distinct banks); with DBUF the tile is double
+// store one chunk into an LDS tile (row pitch KC*2 + kPitchPad bytes, free of
+// bank conflicts for fragment reads); with DBUF the tile is double
 // buffered and each chunk costs one barrier instead of two.  Fragments come
 // from LDS and the accumulators stay in registers.  A strip as wide as the
 // M-block makes re-reading h from L2 cost no more than streaming W.  The
@@ -478,7 +491,7 @@ struct WideCfg {
     static constexpr int KC = 32 * KS;
     static constexpr int MB = 32 * MW;                // rows of h per workgroup
     static constexpr int NB = 16 * WN * NT;           // W rows per strip
-    static constexpr int ROWB = KC * 2 + 16;
+    static constexpr int ROWB = KC * 2 + kPitchPad;
     static constexpr int PIECES = KC / 8;             // 16-byte pieces per row and chunk
     static constexpr int RPL = THREADS / PIECES;      // rows per workgroup-wide load
     static constexpr int HLOADS = (MB + RPL - 1) / RPL;
