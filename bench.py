@@ -5,7 +5,10 @@ One step = one cycle tail over one batch of synthetic inputs resident in HBM:
 five two-tap conv calls (one per drafter layer), the LM head with top-16, the
 pair selector, and verification (greedy, sampled, or half of each), each a
 C-ABI call on one stream.  Inputs rotate over enough copies to exceed the
-256 MB Infinity Cache, so every step streams its inputs from HBM.
+256 MB Infinity Cache, so every step streams its inputs from HBM.  The cycles
+are timed twice: launched eagerly (with per-stage events) and replayed from
+one captured HIP graph per input set (the reported value; the replayed outputs
+are checked to equal the eager ones).
 
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
@@ -70,6 +73,7 @@ class CycleRunner:
     """Pre-bound C-ABI calls for every rotating input set."""
 
     def __init__(self, dfl, torch, cfg, sets, W, F_l, F_r):
+        self.dfl = dfl
         dev = W.device
         B, T, P, L = cfg.B, cfg.T, cfg.P, cfg.L
         self.cfg = cfg
@@ -90,19 +94,45 @@ class CycleRunner:
         self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
         self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
                                 device=dev)
-        tv3, ti3 = self.tv.view(B, P, 16), self.ti.view(B, P, 16)
-        self.calls = []
-        for s in sets:
-            conv = [dfl.bind_conv2tap(s["x"][l], s["taps"][l], self.y[l]) for l in range(L)]
-            head = dfl.bind_head_topk(s["h"], W, self.tv, self.ti, self.ws_head)
-            sel = dfl.bind_select_path(tv3, ti3, F_l, F_r, self.rank, self.tok, self.score, self.ws_sel)
-            ver = []
-            if g > 0:
-                ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
-            if g < B:
-                ver.append(dfl.bind_verify_sample(s["target_s"], self.tok[g:], cfg.temperature, cfg.seed,
-                                                  s["rid_s"], s["pos_s"], self.out[g:], self.n[g:], self.ws_s))
-            self.calls.append((conv, head, sel, ver))
+        self.F_l, self.F_r, self.W = F_l, F_r, W
+        self.sets = sets
+        self.calls = [self.bind_set(s) for s in sets]
+
+    def bind_set(self, s):
+        """The cycle's C-ABI calls on input set s, bound to the current stream."""
+        dfl, cfg, B, L, g = self.dfl, self.cfg, self.cfg.B, self.cfg.L, self.g
+        tv3, ti3 = self.tv.view(B, cfg.P, 16), self.ti.view(B, cfg.P, 16)
+        conv = [dfl.bind_conv2tap(s["x"][l], s["taps"][l], self.y[l]) for l in range(L)]
+        head = dfl.bind_head_topk(s["h"], self.W, self.tv, self.ti, self.ws_head)
+        sel = dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel)
+        ver = []
+        if g > 0:
+            ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
+        if g < B:
+            ver.append(dfl.bind_verify_sample(s["target_s"], self.tok[g:], cfg.temperature, cfg.seed,
+                                              s["rid_s"], s["pos_s"], self.out[g:], self.n[g:], self.ws_s))
+        return conv, head, sel, ver
+
+    def capture(self):
+        """One HIP graph per input set holding that set's whole cycle."""
+        torch = self.torch
+        graphs = []
+        for s in self.sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                conv, head, sel, ver = self.bind_set(s)
+                for c in conv:
+                    c()
+                head()
+                sel()
+                for v in ver:
+                    v()
+            graphs.append(g)
+        return graphs
+
+    def outputs(self):
+        return {"y": [y.cpu() for y in self.y], "ti": self.ti.cpu().numpy(), "tv": self.tv.cpu().numpy(),
+                "tok": self.tok.cpu().numpy(), "out": self.out.cpu().numpy(), "n": self.n.cpu().numpy()}
 
     def run(self, i, ev=None):
         conv, head, sel, ver = self.calls[i % len(self.calls)]
@@ -264,20 +294,42 @@ def main():
     log(f"[bench] {args.steps} cycles in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.1f} us/cycle; head {head_us:.1f} us")
 
-    # outputs of the last cycle on set 0, for the parity check
+    # outputs of one eager cycle on set 0, for the parity check
     runner.run(0)
     torch.cuda.synchronize()
-    gpu_res = {"y": [y.cpu() for y in runner.y], "ti": runner.ti.cpu().numpy(),
-               "tok": runner.tok.cpu().numpy(), "out": runner.out.cpu().numpy(), "n": runner.n.cpu().numpy()}
+    gpu_res = runner.outputs()
+
+    # the same cycles replayed from HIP graphs (one graph per input set)
+    graphs = runner.capture()
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    g_start = torch.cuda.Event(enable_timing=True)
+    g_end = torch.cuda.Event(enable_timing=True)
+    g_start.record(stream)
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    g_end.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = g_start.elapsed_time(g_end) / args.steps
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    g_res = runner.outputs()
+    graph_same = (all(torch.equal(a, b) for a, b in zip(g_res["y"], gpu_res["y"])) and
+                  all(np.array_equal(g_res[k], gpu_res[k]) for k in ("ti", "tv", "tok", "out", "n")))
+    log(f"[bench] graph replay: {ms_graph * 1e3:.1f} us/cycle (eager {ms_per_step * 1e3:.1f}); "
+        f"outputs identical to eager: {graph_same}")
+    if not graph_same:
+        sys.exit("graph replay outputs differ from the eager cycle")
 
     rec = {
         "metric": "draft-verify cycles/sec at block 8, batch 1/8/32; % of HBM/MFMA roofline",
-        "value": round(1e3 / ms_per_step, 2),
+        "value": round(1e3 / ms_graph, 2),
         "unit": "cycles/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(ms_graph, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -291,7 +343,9 @@ def main():
                       "head_topk": round(float(np.median(stage[:, 1])), 2),
                       "select_path": round(float(np.median(stage[:, 2])), 2),
                       "verify": round(float(np.median(stage[:, 3])), 2)},
-        "cycle_us_p10_p50_p90": [round(float(np.percentile(cycle_us, q)), 2) for q in (10, 50, 90)],
+        "launch": "one HIP graph per input set, replayed (eager launches measured as well)",
+        "eager_cycles_per_s": round(1e3 / ms_per_step, 2),
+        "eager_cycle_us_p10_p50_p90": [round(float(np.percentile(cycle_us, q)), 2) for q in (10, 50, 90)],
         "mean_n_emit": round(float(gpu_res["n"].mean()), 3),
     }
     if not args.no_cpu_baseline:
