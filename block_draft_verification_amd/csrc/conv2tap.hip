@@ -6,12 +6,13 @@
 // Reading: y[s][t][c] = a*x[s][t][c] + b*x[s][t-1][c], x[s][-1][c] = 0, with a,
 // b the token's own taps (taps[s][t][0:D] and taps[s][t][D:2D]).
 //
-// Layout and mapping: one thread owns eight channels (one 16-byte vector) of
-// one sequence and walks its T slots, so x is read from HBM exactly once and
-// x[t-1] comes from a register.  Consecutive threads own consecutive 16-byte
-// vectors of the same row: every load and store of a wavefront covers 1 KiB of
-// contiguous memory.  All 3T loads of a thread are issued before any math.
-// HBM traffic per element: x 2 B + taps 4 B + y 2 B.
+// Layout and mapping: one thread per (token row, eight channels), i.e. every
+// wavefront covers 1 KiB of contiguous channels of one token row, and a
+// launch has S*T*D/8 threads, enough to keep the whole chip's memory queues
+// full even for a single sequence.  A thread reads its row's x and taps and
+// the previous row's x (the same bytes the neighbouring thread reads as its
+// own x, so that read hits the cache).  Algorithmic HBM traffic per element:
+// x 2 B + taps 4 B + y 2 B.
 //
 // Arithmetic: bf16 x bf16 products are exact in float32, so fmaf(a, x, b*xp)
 // rounds the exact sum once; the result is rounded to bf16 nearest-even.
@@ -32,57 +33,40 @@ __device__ __forceinline__ uint32_t conv_pair(uint32_t xw, uint32_t aw, uint32_t
     return f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
 }
 
-template <int TMAX>
 __global__ __launch_bounds__(256) void conv2tap_kernel(const u32x4* __restrict__ x,
                                                        const u32x4* __restrict__ taps,
-                                                       u32x4* __restrict__ y,
-                                                       int64_t n_seq, int T, int D8) {
+                                                       u32x4* __restrict__ y, int64_t n_rows, int T, int D8) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= n_seq * D8) return;
-    const int64_t s = gid / D8;
-    const int c8 = (int)(gid - s * D8);
-    const u32x4* xs = x + s * T * D8 + c8;
-    const u32x4* ts = taps + s * T * 2 * D8 + c8;
-    u32x4* ys = y + s * T * D8 + c8;
-
-    u32x4 xv[TMAX], av[TMAX], bv[TMAX];
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-            xv[t] = __builtin_nontemporal_load(xs + (int64_t)t * D8);
-            av[t] = __builtin_nontemporal_load(ts + (int64_t)t * 2 * D8);
-            bv[t] = __builtin_nontemporal_load(ts + (int64_t)t * 2 * D8 + D8);
-        }
-    }
-    float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < TMAX; ++t) {
-        if (t < T) {
-            u32x4 o;
-            o.x = conv_pair(xv[t].x, av[t].x, bv[t].x, p[0], p[1]);
-            o.y = conv_pair(xv[t].y, av[t].y, bv[t].y, p[2], p[3]);
-            o.z = conv_pair(xv[t].z, av[t].z, bv[t].z, p[4], p[5]);
-            o.w = conv_pair(xv[t].w, av[t].w, bv[t].w, p[6], p[7]);
-            __builtin_nontemporal_store(o, ys + (int64_t)t * D8);
-        }
-    }
+    if (gid >= n_rows * D8) return;
+    const int64_t row = gid / D8;  // s * T + t
+    const int c8 = (int)(gid - row * D8);
+    const int t = (int)(row % T);
+    const u32x4 xv = x[row * D8 + c8];
+    const u32x4 av = __builtin_nontemporal_load(taps + row * 2 * D8 + c8);
+    const u32x4 bv = __builtin_nontemporal_load(taps + row * 2 * D8 + D8 + c8);
+    const u32x4 pv = t > 0 ? x[(row - 1) * D8 + c8] : u32x4{0u, 0u, 0u, 0u};
+    float p[8];
+    p[0] = bf16_to_f32(pv.x & 0xFFFFu), p[1] = bf16_to_f32(pv.x >> 16);
+    p[2] = bf16_to_f32(pv.y & 0xFFFFu), p[3] = bf16_to_f32(pv.y >> 16);
+    p[4] = bf16_to_f32(pv.z & 0xFFFFu), p[5] = bf16_to_f32(pv.z >> 16);
+    p[6] = bf16_to_f32(pv.w & 0xFFFFu), p[7] = bf16_to_f32(pv.w >> 16);
+    u32x4 o;
+    o.x = conv_pair(xv.x, av.x, bv.x, p[0], p[1]);
+    o.y = conv_pair(xv.y, av.y, bv.y, p[2], p[3]);
+    o.z = conv_pair(xv.z, av.z, bv.z, p[4], p[5]);
+    o.w = conv_pair(xv.w, av.w, bv.w, p[6], p[7]);
+    __builtin_nontemporal_store(o, y + row * D8 + c8);
 }
 
 int launch_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y, int64_t n_seq,
                     int T, int D, hipStream_t stream) {
     const int D8 = D / 8;
-    const int64_t threads = n_seq * D8;
+    const int64_t n_rows = n_seq * T;
     const int block = 256;
-    const int64_t grid = (threads + block - 1) / block;
-    const u32x4* xp = reinterpret_cast<const u32x4*>(x);
-    const u32x4* tp = reinterpret_cast<const u32x4*>(taps);
-    u32x4* yp = reinterpret_cast<u32x4*>(y);
-    if (T <= 4)
-        hipLaunchKernelGGL(conv2tap_kernel<4>, dim3((unsigned)grid), dim3(block), 0, stream, xp, tp, yp, n_seq, T, D8);
-    else if (T <= 8)
-        hipLaunchKernelGGL(conv2tap_kernel<8>, dim3((unsigned)grid), dim3(block), 0, stream, xp, tp, yp, n_seq, T, D8);
-    else
-        hipLaunchKernelGGL(conv2tap_kernel<16>, dim3((unsigned)grid), dim3(block), 0, stream, xp, tp, yp, n_seq, T, D8);
+    const int64_t grid = (n_rows * D8 + block - 1) / block;
+    hipLaunchKernelGGL(conv2tap_kernel, dim3((unsigned)grid), dim3(block), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(taps),
+                       reinterpret_cast<u32x4*>(y), n_rows, T, D8);
     return launch_status();
 }
 

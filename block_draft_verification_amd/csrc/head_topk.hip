@@ -722,6 +722,26 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Wavefront sum of a double (the result is complete in lane 63): row-level
+// Hillis-Steele with DPP row shifts, then row broadcasts.  Lanes whose DPP
+// source falls outside the row add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_add_f64(double x) {
+    const uint64_t u = __double_as_longlong(x);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, ROW_MASK, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+    return x + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    x = dpp_add_f64<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_add_f64<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_add_f64<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_add_f64<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_add_f64<0x142, 0xA>(x);  // row_bcast:15
+    x = dpp_add_f64<0x143, 0xC>(x);  // row_bcast:31
+    return x;
+}
+
 // Pop the kRescore best entries of up to 64 sorted lists of length len held
 // in LDS (list l of lane l at lv/li + l * len); results to ov/oi.
 __device__ __forceinline__ void extract_top(const float* lv, const int* li, int len, int nlists, float* ov,
@@ -834,23 +854,27 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
                 }
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            acc0 += __shfl_xor(acc0, off);
-            acc1 += __shfl_xor(acc1, off);
-        }
-        if (lane == 0) {
+        acc0 = wave_sum_f64(acc0);
+        acc1 = wave_sum_f64(acc1);
+        if (lane == 63) {
             sel_z[c0] = acc0;
             if (has1) sel_z[c1] = acc1;
         }
     }
     __syncthreads();
-    if (tid < ns) {
+    if (wave == 0) {
+        // lane t < ns holds candidate t; its rank = the candidates before it
+        const double z = lane < ns ? sel_z[lane] : 0.0;
+        const int id = lane < ns ? sel_i[lane] : 0x7FFFFFFF;
         int rank = 0;
-        for (int t = 0; t < ns; ++t) rank += ranks_before_d(sel_z[t], sel_i[t], sel_z[tid], sel_i[tid]) ? 1 : 0;
-        if (rank < kTopK) {
-            top_val[m * kTopK + rank] = (float)sel_z[tid];
-            top_idx[m * kTopK + rank] = sel_i[tid];
+        for (int t = 0; t < ns; ++t) {
+            const double zt = __shfl(z, t);
+            const int it = __shfl(id, t);
+            rank += ranks_before_d(zt, it, z, id) ? 1 : 0;
+        }
+        if (lane < ns && rank < kTopK) {
+            top_val[m * kTopK + rank] = (float)z;
+            top_idx[m * kTopK + rank] = id;
         }
     }
 }

@@ -20,6 +20,7 @@
 
 namespace dflash {
 
+
 constexpr int kChunk = 4096;
 constexpr int kVerifyThreads = 256;
 constexpr int kPerThread = kChunk / kVerifyThreads;  // 16
