@@ -22,8 +22,8 @@
 //   W rows and the h rows row-contiguously with buffer loads (two chunks of
 //   32*KS columns in flight), stages them in its private LDS tile, multiplies
 //   from there, and keeps its own running top-16 per row in LDS.  No barrier
-//   inside the stream.  At the end the four wavefronts of a workgroup merge
-//   their lists.
+//   inside the stream.  At the end the wavefronts of a workgroup merge their
+//   lists.
 // * head_wide_kernel (M > 16): a workgroup of 2 x WN wavefronts owns an
 //   M-block of 32*MW rows of h and a contiguous range of vocabulary tiles,
 //   walked in strips of 16*NT*WN rows.  Per chunk of the hidden dimension the
@@ -424,44 +424,79 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
     topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, t0 * 16, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
 }
 
-template <int NT, int KS>
-__global__ __launch_bounds__(256) void head_skinny2_kernel(const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ W, int64_t M,
-                                                           int D, int64_t V, int64_t n_tiles,
-                                                           float* __restrict__ part_val,
-                                                           int* __restrict__ part_idx) {
+// WAVES wavefronts per workgroup (4 or 8).
+template <int NT, int KS, int WAVES>
+struct SkinnyLds {
     using C = Skinny2Cfg<NT, KS>;
-    __shared__ __align__(16) unsigned char s_w[4][C::LDS_W];
-    __shared__ float s_lval[4][16 * kTopK];
-    __shared__ int s_lidx[4][16 * kTopK];
-    __shared__ float s_cval[4][16 * kCap];
-    __shared__ int s_cidx[4][16 * kCap];
-    __shared__ __align__(16) float s_thr[4][16];
-    __shared__ __align__(16) int s_thri[4][16];
-    __shared__ int s_ccnt[4][16];
+    static constexpr size_t TILES = (size_t)WAVES * C::LDS_W;
+    static constexpr size_t LISTS = (size_t)WAVES * 16 * (kTopK * 8 + kCap * 8 + 12);
+    static constexpr size_t BYTES = TILES + LISTS;
+    static_assert(BYTES <= 160 * 1024, "LDS per workgroup");
+};
 
-    const int wave = threadIdx.x >> 6;
+template <int NT, int KS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t* __restrict__ h,
+                                                                 const uint16_t* __restrict__ W, int64_t M,
+                                                                 int D, int64_t V, int64_t n_tiles,
+                                                                 float* __restrict__ part_val,
+                                                                 int* __restrict__ part_idx) {
+    using C = Skinny2Cfg<NT, KS>;
+    using Lds = SkinnyLds<NT, KS, WAVES>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    TopkRows tk{s_lval[wave], s_lidx[wave], s_cval[wave], s_cidx[wave], s_thr[wave], s_thri[wave], s_ccnt[wave]};
+    unsigned char* s_w = smem + (size_t)wave * C::LDS_W;
+    // per-wavefront list state: lval, lidx [16][16]; cval, cidx [16][kCap]; thr, thri, ccnt [16]
+    auto lists = [&](int w) { return smem + Lds::TILES + (size_t)w * 16 * (kTopK * 8 + kCap * 8 + 12); };
+    auto make_rows = [&](int w) {
+        unsigned char* b = lists(w);
+        TopkRows t;
+        t.lval = reinterpret_cast<float*>(b);
+        t.lidx = reinterpret_cast<int*>(b + 16 * kTopK * 4);
+        t.cval = reinterpret_cast<float*>(b + 16 * kTopK * 8);
+        t.cidx = reinterpret_cast<int*>(b + 16 * kTopK * 8 + 16 * kCap * 4);
+        t.thr = reinterpret_cast<float*>(b + 16 * kTopK * 8 + 16 * kCap * 8);
+        t.thri = reinterpret_cast<int*>(t.thr + 16);
+        t.ccnt = t.thri + 16;
+        return t;
+    };
+    TopkRows tk = make_rows(wave);
     topk_init(tk, 16, lane, 64);
     wave_sync();
 
-    const int64_t nw = (int64_t)gridDim.x * 4;
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * WAVES;
+    const int64_t gw = (int64_t)blockIdx.x * WAVES + wave;
     const int64_t t_begin = gw * n_tiles / nw, t_end = (gw + 1) * n_tiles / nw;
     const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(h, M * D * 2);
 
     int64_t t0 = t_begin;
-    for (; t0 + NT <= t_end; t0 += NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, V, t0, tk, s_w[wave]);
-    for (; t0 < t_end; ++t0) skinny2_tiles<1, KS>(hsrc, W, M, D, V, t0, tk, s_w[wave]);
+    for (; t0 + NT <= t_end; t0 += NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, V, t0, tk, s_w);
+    for (; t0 < t_end; ++t0) skinny2_tiles<1, KS>(hsrc, W, M, D, V, t0, tk, s_w);
 
+    // workgroup list per row: the wavefronts' lists merged in groups of four
+    // (a 64-lane sort each), then the groups' leaders (a 32-lane sort)
     __syncthreads();
+    static_assert(WAVES == 4 || WAVES == 8, "4 or 8 wavefronts");
     const int S = gridDim.x;
-    for (int r = wave; r < min<int64_t>(M, 16); r += 4) {
+    for (int r = wave; r < min<int64_t>(M, 16); r += WAVES) {
         const int src = lane >> 4, k = lane & 15;
-        float v = s_lval[src][r * kTopK + k];
-        int ix = s_lidx[src][r * kTopK + k];
+        TopkRows ta = make_rows(src);
+        float v = ta.lval[r * kTopK + k];
+        int ix = ta.lidx[r * kTopK + k];
         bitonic_desc<64>(v, ix);
+        if (WAVES == 8) {
+            TopkRows tb = make_rows(4 + src);
+            float vb = tb.lval[r * kTopK + k];
+            int ib = tb.lidx[r * kTopK + k];
+            bitonic_desc<64>(vb, ib);
+            const float vs = __shfl(vb, lane & 15);
+            const int is = __shfl(ib, lane & 15);
+            if (lane >= 16 && lane < 32) {
+                v = vs;
+                ix = is;
+            }
+            bitonic_desc<32>(v, ix);
+        }
         if (lane < kTopK) {
             const int64_t o = ((int64_t)r * S + blockIdx.x) * kTopK + lane;
             part_val[o] = v;
@@ -908,7 +943,9 @@ struct WideVariant {
     }
 };
 
-constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWG = 512;  // 2 workgroups (8 wavefronts) per CU
+// two workgroups of four wavefronts per CU (measured faster than one of eight)
+constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWaves = 4, kSkinnyWG = 512;
+using SkinnyL = SkinnyLds<kSkinnyNT, kSkinnyKS, kSkinnyWaves>;
 // Measured on MI355X (V = 151936, D = 5120) among the register-feasible
 // instantiations: 8 wavefronts with 64x32 / 112x32 wavefront tiles.
 using Wide128 = WideVariant<4, 2, 2, 4, true, 4>;  // M-blocks of 128 rows
@@ -922,7 +959,7 @@ HeadPlan head_plan(int64_t M, int64_t V) {
         p.variant = kSkinny;
         p.mb_rows = 16;
         p.n_mb = 1;
-        const int64_t want = (p.n_tiles + 3) / 4;  // at least one tile per wavefront
+        const int64_t want = (p.n_tiles + kSkinnyWaves - 1) / kSkinnyWaves;  // at least one tile per wavefront
         p.S = (int)std::min<int64_t>(kSkinnyWG, want);
         return p;
     }
@@ -953,6 +990,9 @@ size_t head_workspace_bytes(int64_t M, int64_t V) {
 int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
                      float* top_val, int32_t* top_idx, void* ws, hipStream_t stream) {
     std::call_once(g_head_attr_once, []() {
+        (void)hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkinnyL::BYTES);
         Wide128::set_attr();
         Wide224::set_attr();
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
@@ -963,7 +1003,8 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
     int* pi = reinterpret_cast<int*>(pv + (size_t)M * p.S * kTopK);
     switch (p.variant) {
         case kSkinny:
-            hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS>), dim3(p.S), dim3(256), 0, stream, h, W, M,
+            hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves>), dim3(p.S),
+                               dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M,
                                D, V, p.n_tiles, pv, pi);
             break;
         case kWide128:
