@@ -103,3 +103,59 @@ def test_reruns_bit_identical(dfl, dev):
     b = gpu_cycle(dfl, inp, cfg)
     for k in ("top_val", "top_idx", "path_rank", "path_score", "out_tok", "n_emit"):
         assert torch.equal(a[k], b[k]), k
+
+
+def _conv_rows_match(res, inp, seqs):
+    from oracle.conv import conv2tap as oconv
+    for l in range(len(res["y"])):
+        ref = oconv(inp["x"][l][seqs].cpu(), inp["taps"][l][seqs].cpu())
+        assert torch.equal(res["y"][l][seqs].cpu().view(torch.int16), ref.view(torch.int16)), l
+
+
+def test_stagewise_batch32_mixed(dfl, dev):
+    """Batch 32 at the full shapes, requests 0-15 greedy and 16-31 sampled:
+    conv on sampled sequences, the head on sampled rows, then the selector and
+    both verifiers exactly, each fed the GPU's previous stage."""
+    cfg = get_config("c4_b32")
+    inp = make_cycle_inputs(cfg, device=dev)
+    res = gpu_cycle(dfl, inp, cfg)
+    _conv_rows_match(res, inp, [0, 17, 31])
+    rows = [0, 111, 223]
+    rv, ri, _ = oracle_topk(inp["h"].cpu(), inp["W"].cpu(), rows=rows)
+    assert np.array_equal(res["top_idx"].view(-1, 16).cpu().numpy()[rows], ri)
+    assert np.array_equal(res["top_val"].view(-1, 16).cpu().numpy()[rows], rv)
+    r0, t0, s0, _ = oracle_select(res["top_val"].cpu().numpy(), res["top_idx"].cpu().numpy(),
+                                  inp["F_l"].cpu(), inp["F_r"].cpu())
+    assert np.array_equal(res["path_rank"].cpu().numpy(), r0)
+    assert np.array_equal(res["path_tok"].cpu().numpy(), t0)
+    assert np.array_equal(res["path_score"].cpu().numpy(), s0)
+    h = cfg.B // 2
+    tok = res["path_tok"].cpu()
+    o0, n0 = og(inp["target"][:h].cpu(), tok[:h])
+    o1, n1 = osamp(inp["target"][h:].cpu(), tok[h:], cfg.temperature, cfg.seed,
+                   inp["request_id"][h:].cpu(), inp["pos0"][h:].cpu())
+    assert np.array_equal(res["out_tok"].cpu().numpy(), np.concatenate([o0, o1]))
+    assert np.array_equal(res["n_emit"].cpu().numpy(), np.concatenate([n0, n1]))
+
+
+def test_stagewise_stress_context_copy(dfl, dev):
+    """Batch 32, block 16, vocabulary 262144, context-copy targets: head rows
+    sampled, selector and greedy verify exact against the oracle fed the GPU's
+    previous stage; with exact 80 % agreement on the planted tokens the
+    accepted lengths are long."""
+    cfg = get_config("c5_stress")
+    inp = make_cycle_inputs(cfg, device=dev)
+    res = gpu_cycle(dfl, inp, cfg)
+    _conv_rows_match(res, inp, [3, 30])
+    rows = [5, 479]
+    rv, ri, _ = oracle_topk(inp["h"].cpu(), inp["W"].cpu(), rows=rows)
+    assert np.array_equal(res["top_idx"].view(-1, 16).cpu().numpy()[rows], ri)
+    assert np.array_equal(res["top_val"].view(-1, 16).cpu().numpy()[rows], rv)
+    r0, t0, s0, _ = oracle_select(res["top_val"].cpu().numpy(), res["top_idx"].cpu().numpy(),
+                                  inp["F_l"].cpu(), inp["F_r"].cpu())
+    assert np.array_equal(res["path_tok"].cpu().numpy(), t0)
+    assert np.array_equal(res["path_score"].cpu().numpy(), s0)
+    o0, n0 = og(inp["target"].cpu(), res["path_tok"].cpu())
+    assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
+    assert np.array_equal(res["n_emit"].cpu().numpy(), n0)
+    assert res["n_emit"].float().mean().item() > 3.0
