@@ -723,39 +723,19 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
 // ---------------------------------------------------------------- merge
 // One workgroup of 10 wavefronts per row.
 // (1) The row's S sorted partial lists (S <= kMaxLists) are copied to LDS.
-// (2) k-way extraction: a wavefront takes 64 lists (one per lane), and 20
-//     times pops the best of the 64 list heads (wavefront arg-max; the winning
-//     lane advances in its list) -> a sorted top-20 per group of 64 lists.
-// (3) One wavefront extracts the top 20 of the group results the same way.
-// (4) Each wavefront re-scores two of those 20 exactly: all loads of the h
+// (2) Threshold selection: T = the 20th-best list head; the entries at or
+//     above T (a prefix of each list) are gathered and sorted by one
+//     wavefront.  (If there are more than 64 of them: k-way extraction, where
+//     a wavefront takes 64 lists and 20 times pops the best list head, and
+//     one wavefront then pops the best 20 of the group results.)
+// (3) Each wavefront re-scores two of those 20 exactly: all loads of the h
 //     row and both W rows are issued before any arithmetic (one HBM round
 //     trip); bf16 products are exact in float64 and summed in float64.
-// (5) Rank by the exact value (ties: lower id) and write the best 16.
+// (4) Rank by the exact value (ties: lower id) and write the best 16.
 constexpr int kMaxLists = 1024;
 constexpr int kMergeSeg = 10;  // 16-byte pieces per lane per pass over D
 
 
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t x) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, ROW_MASK, 0xF, true);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(x >> 32), CTRL, ROW_MASK, 0xF, true);
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    return y > x ? y : x;
-}
-
-// Wavefront maximum of a 64-bit key with DPP row shifts and row broadcasts;
-// every lane gets the result.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-    x = dpp_max_u64<0x111, 0xF>(x);  // row_shr:1
-    x = dpp_max_u64<0x112, 0xF>(x);  // row_shr:2
-    x = dpp_max_u64<0x114, 0xF>(x);  // row_shr:4
-    x = dpp_max_u64<0x118, 0xF>(x);  // row_shr:8
-    x = dpp_max_u64<0x142, 0xA>(x);  // row_bcast:15
-    x = dpp_max_u64<0x143, 0xC>(x);  // row_bcast:31
-    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)x, 63);
-    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(x >> 32), 63);
-    return ((uint64_t)hi << 32) | lo;
-}
 
 // Wavefront sum of a double (the result is complete in lane 63): row-level
 // Hillis-Steele with DPP row shifts, then row broadcasts.  Lanes whose DPP
@@ -777,8 +757,64 @@ __device__ __forceinline__ double wave_sum_f64(double x) {
     return x;
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Lane ^ m for any m: DPP inside 16-lane rows where one exists, else a permute.
+template <int M>
+__device__ __forceinline__ uint64_t xor_lane_u64(uint64_t k, int lane) {
+    if constexpr (M == 1) return dpp_u64<kDppX1>(k);
+    else if constexpr (M == 2) return dpp_u64<kDppX2>(k);
+    else if constexpr (M == 3) return dpp_u64<kDppX3>(k);
+    else if constexpr (M == 4) return xor4_u64(k, lane & 15);
+    else if constexpr (M == 7) return dpp_u64<kDppX7>(k);
+    else if constexpr (M == 8) return dpp_u64<kDppX8>(k);
+    else if constexpr (M == 15) return dpp_u64<kDppX15>(k);
+    else return shfl_xor_u64(k, M);
+}
+// Bitonic sort of one key per lane across the wavefront, descending: merge
+// stages start with the mirrored comparison (lane ^ (2s - 1)), so every block
+// sorts in the same direction.
+template <int S2 = 1>
+__device__ __forceinline__ uint64_t sort64_stage(uint64_t k, int lane) {
+    if constexpr (S2 < 64) {
+        k = cx(k, xor_lane_u64<2 * S2 - 1>(k, lane), (lane & S2) == 0);
+        if constexpr (S2 >= 32) k = cx(k, xor_lane_u64<16>(k, lane), (lane & 16) == 0);
+        if constexpr (S2 >= 16) k = cx(k, xor_lane_u64<8>(k, lane), (lane & 8) == 0);
+        if constexpr (S2 >= 8) k = cx(k, xor_lane_u64<4>(k, lane), (lane & 4) == 0);
+        if constexpr (S2 >= 4) k = cx(k, xor_lane_u64<2>(k, lane), (lane & 2) == 0);
+        if constexpr (S2 >= 2) k = cx(k, xor_lane_u64<1>(k, lane), (lane & 1) == 0);
+        return sort64_stage<S2 * 2>(k, lane);
+    } else {
+        return k;
+    }
+}
+__device__ __forceinline__ uint64_t sort64_desc(uint64_t k, int lane) { return sort64_stage<1>(k, lane); }
+
+// Wavefront maximum of a float (every lane gets it): DPP row shifts, row
+// broadcasts and a read of lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_f32(float x) {
+    return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(-INFINITY), __float_as_int(x), CTRL,
+                                                               ROW_MASK, 0xF, false)));
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+    x = dpp_max_f32<0x111, 0xF>(x);  // row_shr:1
+    x = dpp_max_f32<0x112, 0xF>(x);  // row_shr:2
+    x = dpp_max_f32<0x114, 0xF>(x);  // row_shr:4
+    x = dpp_max_f32<0x118, 0xF>(x);  // row_shr:8
+    x = dpp_max_f32<0x142, 0xA>(x);  // row_bcast:15
+    x = dpp_max_f32<0x143, 0xC>(x);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // Pop the kRescore best entries of up to 64 sorted lists of length len held
-// in LDS (list l of lane l at lv/li + l * len); results to ov/oi.
+// in LDS (list l of lane l at lv/li + l * len); results to ov/oi.  A pop
+// takes the wavefront maximum of the list heads' values; when several lanes
+// hold that value (ties, or only sentinels left) the lowest id among them
+// wins, so the order is the ranks_before order.
 __device__ __forceinline__ void extract_top(const float* lv, const int* li, int len, int nlists, float* ov,
                                             int* oi) {
     const int lane = threadIdx.x & 63;
@@ -786,21 +822,26 @@ __device__ __forceinline__ void extract_top(const float* lv, const int* li, int 
     float hv = lane < nlists ? lv[lane * len] : -INFINITY;
     int hi = lane < nlists ? li[lane * len] : 0x7FFFFFFF;
     for (int k = 0; k < kRescore; ++k) {
-        const uint64_t mine = rank_key(hv, hi);
-        const uint64_t best = wave_max_u64(mine);
-        // The winner is unique (distinct ids) unless only sentinels are left;
-        // then every lane ties and the first writes a sentinel.  Only lanes
-        // that own a list advance, and never past its end.
-        if (mine == best) {
-            if (lane == __builtin_amdgcn_readfirstlane(lane)) {
-                ov[k] = hv;
-                oi[k] = hi;
-            }
-            if (lane < nlists && pos < len) {
-                ++pos;
-                hv = pos < len ? lv[lane * len + pos] : -INFINITY;
-                hi = pos < len ? li[lane * len + pos] : 0x7FFFFFFF;
-            }
+        const float best = wave_max_f32(hv);
+        const uint64_t at = __ballot(hv == best);
+        int win = __ffsll((unsigned long long)at) - 1;
+        int wid = __shfl(hi, win);
+        if (__popcll(at) > 1) {  // ties: lowest id among the lanes at the maximum
+            int mid = hv == best ? hi : 0x7FFFFFFF;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) mid = min(mid, __shfl_xor(mid, off));
+            wid = mid;
+            win = __ffsll((unsigned long long)__ballot(hv == best && hi == mid)) - 1;
+        }
+        if (lane == 0) {
+            ov[k] = best;
+            oi[k] = wid;
+        }
+        // only a lane that owns a list advances, and never past its end
+        if (lane == win && lane < nlists && pos < len) {
+            ++pos;
+            hv = pos < len ? lv[lane * len + pos] : -INFINITY;
+            hi = pos < len ? li[lane * len + pos] : 0x7FFFFFFF;
         }
     }
 }
@@ -817,6 +858,11 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
     __shared__ float sel_v[kRescore];
     __shared__ int sel_i[kRescore];
     __shared__ double sel_z[kRescore];
+    __shared__ unsigned long long hk[kMaxLists];             // list heads
+    __shared__ unsigned long long gh[kMaxLists / 64][32];    // per group: its 32 best heads
+    __shared__ unsigned long long cand[64];
+    __shared__ unsigned long long s_thr;
+    __shared__ int s_count;
 
     const int64_t m = blockIdx.x;
     const int tid = threadIdx.x;
@@ -844,11 +890,74 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
         }
     }
     __syncthreads();
-    const int ng = (S + 63) / 64;
-    for (int g = wave; g < ng; g += kMergeThreads / 64)
-        extract_top(lv + g * 64 * kTopK, li + g * 64 * kTopK, kTopK, min(64, S - g * 64), gv[g], gi[g]);
+    // (2) T = the smallest of the kRescore largest list heads: at least
+    // kRescore entries rank at or above T, so every entry of the row's best
+    // kRescore does too.  Candidates = the entries at or above T (a prefix of
+    // each sorted list), usually a few dozen; up to 64 are sorted by one
+    // wavefront, more fall back to k-way extraction.
+    // (With fewer than kRescore lists the heads do not bound anything: T is
+    // the empty key and every entry is a candidate.)
+    if (tid == 0) {
+        s_thr = S < kRescore ? kEmptyKey : ~0ull;
+        s_count = 0;
+    }
+    for (int t = tid; t < S; t += kMergeThreads) hk[t] = rank_key(lv[t * kTopK], li[t * kTopK]);
     __syncthreads();
-    if (wave == 0) extract_top(&gv[0][0], &gi[0][0], kRescore, ng, sel_v, sel_i);
+    // the 20 best heads: each group of 64 heads sorted by one wavefront, then
+    // the groups' leading 32 merged pairwise
+    const int ng = (S + 63) / 64;
+    if (S >= kRescore) {
+        for (int g = wave; g < ng; g += kMergeThreads / 64) {
+            const int t = g * 64 + lane;
+            uint64_t k = t < S ? hk[t] : kEmptyKey;
+            k = sort64_desc(k, lane);
+            if (lane < 32) gh[g][lane] = k;
+        }
+    }
+    __syncthreads();
+    for (int span = 1; span < ng && S >= kRescore; span <<= 1) {
+        for (int g = wave * 2 * span; g < ng; g += kMergeThreads / 64 * 2 * span) {
+            if (g + span < ng) {  // merge group g + span into group g
+                uint64_t k = lane < 32 ? gh[g][lane] : gh[g + span][63 - lane];
+                // b enters reversed (ascending) in lanes 32..63: a 64-long bitonic sequence
+                k = cx(k, xor_lane_u64<32>(k, lane), (lane & 32) == 0);
+                k = cx(k, xor_lane_u64<16>(k, lane), (lane & 16) == 0);
+                k = cx(k, xor_lane_u64<8>(k, lane), (lane & 8) == 0);
+                k = cx(k, xor_lane_u64<4>(k, lane), (lane & 4) == 0);
+                k = cx(k, xor_lane_u64<2>(k, lane), (lane & 2) == 0);
+                k = cx(k, xor_lane_u64<1>(k, lane), (lane & 1) == 0);
+                if (lane < 32) gh[g][lane] = k;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid == 0 && S >= kRescore) s_thr = gh[0][kRescore - 1];
+    __syncthreads();
+    const unsigned long long T = s_thr;
+    for (int t = tid; t < S; t += kMergeThreads) {
+        for (int c = 0; c < kTopK; ++c) {
+            const unsigned long long k = rank_key(lv[t * kTopK + c], li[t * kTopK + c]);
+            if (k < T) break;
+            const int pos = atomicAdd(&s_count, 1);
+            if (pos < 64) cand[pos] = k;
+        }
+    }
+    __syncthreads();
+    if (s_count <= 64) {
+        if (wave == 0) {
+            uint64_t k = lane < s_count ? cand[lane] : kEmptyKey;
+            k = sort64_desc(k, lane);
+            if (lane < kRescore) {
+                sel_v[lane] = key_value(k);
+                sel_i[lane] = key_id(k);
+            }
+        }
+    } else {
+        for (int g = wave; g < ng; g += kMergeThreads / 64)
+            extract_top(lv + g * 64 * kTopK, li + g * 64 * kTopK, kTopK, min(64, S - g * 64), gv[g], gi[g]);
+        __syncthreads();
+        if (wave == 0) extract_top(&gv[0][0], &gi[0][0], kRescore, ng, sel_v, sel_i);
+    }
     __syncthreads();
     int ns = 0;
     // real entries precede the sentinels; an id outside [0, V) (none is
