@@ -170,6 +170,11 @@ def make_sets(torch, cfg, inp, max_sets):
     return sets, per_set
 
 
+def head_kernels(cfg):
+    gemm = "head_skinny2_kernel" if cfg.M <= 16 else "head_wide_kernel"
+    return f"dflash_head_topk call = {gemm} + head_merge_kernel (HIP events around the call)"
+
+
 def head_roofline(cfg, head_us):
     flops = 2.0 * cfg.M * cfg.V * cfg.D
     bytes_ = cfg.V * cfg.D * 2 + cfg.M * cfg.D * 2 + cfg.M * 16 * 8
@@ -181,14 +186,12 @@ def head_roofline(cfg, head_us):
         ach = bytes_ / t / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "dflash_head_topk (head_topk_kernel + head_merge_kernel)",
-                "algorithmic_bytes": int(bytes_), "flops": int(flops),
+                "kernel": head_kernels(cfg), "algorithmic_bytes": int(bytes_), "flops": int(flops),
                 "mfma_frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     ach = flops / t / 1e12
     return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-            "kernel": "dflash_head_topk (head_topk_kernel + head_merge_kernel)",
-            "algorithmic_bytes": int(bytes_), "flops": int(flops),
+            "kernel": head_kernels(cfg), "algorithmic_bytes": int(bytes_), "flops": int(flops),
             "hbm_frac": round(bytes_ / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
