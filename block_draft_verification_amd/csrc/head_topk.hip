@@ -1056,7 +1056,9 @@ struct WideVariant {
 constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWaves = 4, kSkinnyWG = 512;
 using SkinnyL = SkinnyLds<kSkinnyNT, kSkinnyKS, kSkinnyWaves>;
 // Measured on MI355X (V = 151936, D = 5120) among the register-feasible
-// instantiations: 8 wavefronts with 64x32 / 112x32 wavefront tiles.
+// instantiations: 8 wavefronts with 64x32 / 112x32 wavefront tiles (e.g. at
+// M = 224: 580-600 us for 224-row blocks, 795 us for two 128-row blocks; at
+// M = 480: 1400 us for four 128-row blocks, 1680 us for three 224-row ones).
 using Wide128 = WideVariant<4, 2, 2, 4, true, 4>;  // M-blocks of 128 rows
 using Wide224 = WideVariant<7, 2, 2, 2, true, 4>;  // M-blocks of 224 rows
 constexpr int kCUs = 256;
@@ -1072,12 +1074,15 @@ HeadPlan head_plan(int64_t M, int64_t V) {
         p.S = (int)std::min<int64_t>(kSkinnyWG, want);
         return p;
     }
-    if (M <= 128) {
+    // the M-block size that pads M the least (224-row blocks win ties: fewer
+    // of them read W)
+    const int64_t pad128 = (M + 127) / 128 * 128, pad224 = (M + 223) / 224 * 224;
+    if (M > 128 && pad224 <= pad128) {
+        p.variant = kWide224;
+        p.mb_rows = Wide224::Cfg::MB;
+    } else {
         p.variant = kWide128;
         p.mb_rows = Wide128::Cfg::MB;
-    } else {
-        p.variant = kWide224;  // M-blocks of 224 rows
-        p.mb_rows = Wide224::Cfg::MB;
     }
     p.n_mb = (int)((M + p.mb_rows - 1) / p.mb_rows);
     // one workgroup per CU (the chunk tile takes most of the LDS)
