@@ -106,6 +106,7 @@ struct TopkRows {
     float* thr;   // [rows] 16th-best value and id
     int* thri;
     int* ccnt;    // [rows] candidates since the last merge
+    uint32_t* seed;  // [rows][16] first-strip threshold seeds (workgroup-shared lists only)
 };
 
 __device__ __forceinline__ void topk_init(TopkRows t, int rows, int tid, int nthreads) {
@@ -198,7 +199,7 @@ __device__ __forceinline__ uint64_t merge16_desc(uint64_t k, int li) {
 template <int MW, int NT, bool WG>
 __device__ __forceinline__ void topk_epilogue(const floatx4 (&acc)[MW][NT], TopkRows t, int rbase, int64_t grow0,
                               int64_t M, int64_t col0, int col_step, int nt_act, int64_t V, int mw_act,
-                              int n_merge_rows, int q0, int q_step) {
+                              int n_merge_rows, int q0, int q_step, bool seed = false) {
     // The empty asm statements make lane, M and rbase opaque at each call, so
     // that nothing derived from them is hoisted out of the caller's tile loop
     // (where it would stay live through the streaming loop and spill).
@@ -207,44 +208,107 @@ __device__ __forceinline__ void topk_epilogue(const floatx4 (&acc)[MW][NT], Topk
     asm volatile("" : "+s"(M));
     asm volatile("" : "+v"(rbase));
     const int ln = lane & 15, lg = lane >> 4;
+    // pending[mt] bit nt * 4 + q: value acc[mt][nt][q] still has to be
+    // offered (initially: every value of a real row and vocabulary id)
     uint32_t pending[MW];
 #pragma unroll
-    for (int mt = 0; mt < MW; ++mt) pending[mt] = 0;
-    bool first = true;
-    while (true) {
+    for (int mt = 0; mt < MW; ++mt) {
+        uint32_t p = 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const bool col_ok = nt < nt_act && col0 + (int64_t)nt * col_step + ln < V;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (col_ok && mt < mw_act && grow0 + mt * 16 + 4 * lg + q < M) p |= 1u << (nt * 4 + q);
+        }
+        pending[mt] = p;
+    }
+    if (WG && seed) {
+        // Threshold seed for lists that are still empty: for each row and lane
+        // position ln, the largest of the values the wavefronts hold there
+        // (distinct columns); the smallest of those 16 maxima is a value that
+        // at least 16 distinct entries of the row reach, hence no greater than
+        // the row's 16th best.  Rows start with it as threshold (id INT_MAX:
+        // any value at least that large stays a candidate), which keeps most of
+        // the first strip out of the merge rounds.
+        for (int e = threadIdx.x; e < n_merge_rows * 16; e += blockDim.x) t.seed[e] = 0u;
+        __syncthreads();
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt) {
-            if (mt < mw_act) {
-                const int r0 = rbase + mt * 16 + 4 * lg;
-                const float4 t4 = *reinterpret_cast<const float4*>(t.thr + r0);
-                const int4 i4 = *reinterpret_cast<const int4*>(t.thri + r0);
-                const float tq[4] = {t4.x, t4.y, t4.z, t4.w};
-                const int iq[4] = {i4.x, i4.y, i4.z, i4.w};
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const int64_t col = col0 + (int64_t)nt * col_step + ln;
+            for (int q = 0; q < 4; ++q) {
+                float m = -INFINITY;
+                bool any = false;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t bit = 1u << (nt * 4 + q);
-                        const bool live = first ? (nt < nt_act && col < V && grow0 + mt * 16 + 4 * lg + q < M)
-                                                : (pending[mt] & bit) != 0;
-                        if (!first) pending[mt] &= ~bit;
-                        const float v = acc[mt][nt][q];
-                        if (live && ranks_before(v, (int)col, tq[q], iq[q])) {
-                            const int r = r0 + q;
-                            const int slot = atomicAdd(&t.ccnt[r], 1);
-                            if (slot < kCap) {
-                                t.cval[r * kCap + slot] = v;
-                                t.cidx[r * kCap + slot] = (int)col;
-                            } else {
-                                pending[mt] |= bit;
-                            }
+                for (int nt = 0; nt < NT; ++nt)
+                    if (pending[mt] & (1u << (nt * 4 + q))) {
+                        m = any ? fmaxf(m, acc[mt][nt][q]) : acc[mt][nt][q];
+                        any = true;
+                    }
+                if (any) atomicMax(&t.seed[(rbase + mt * 16 + 4 * lg + q) * 16 + ln], (uint32_t)(rank_key(m, 0) >> 32));
+            }
+        }
+        __syncthreads();
+        const int li = lane & 15;
+        for (int r = q0 + (lane >> 4); r < n_merge_rows; r += q_step) {
+            uint32_t k = t.seed[r * 16 + li];
+            k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, kDppX1, 0xF, 0xF, true));
+            k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, kDppX2, 0xF, 0xF, true));
+            k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, kDppX7, 0xF, 0xF, true));
+            k = min(k, (uint32_t)__builtin_amdgcn_mov_dpp((int)k, kDppX15, 0xF, 0xF, true));
+            // key 0: some lane position held no value, so no bound
+            if (li == 0 && k > (uint32_t)(kEmptyKey >> 32)) {
+                t.thr[r] = key_value((uint64_t)k << 32);
+                t.thri[r] = 0x7FFFFFFF;
+            }
+        }
+        __syncthreads();
+    }
+    while (true) {
+        // Per 16-row tile: compare every pending value with its row's
+        // threshold, then (only if some lane has a candidate) reserve the
+        // slots with all atomics in flight together, then store.
+#pragma unroll
+        for (int mt = 0; mt < MW; ++mt) {
+            if (__ballot(pending[mt] != 0) == 0) continue;
+            const int r0 = rbase + mt * 16 + 4 * lg;
+            const float4 t4 = *reinterpret_cast<const float4*>(t.thr + r0);
+            const int4 i4 = *reinterpret_cast<const int4*>(t.thri + r0);
+            const float tq[4] = {t4.x, t4.y, t4.z, t4.w};
+            const int iq[4] = {i4.x, i4.y, i4.z, i4.w};
+            uint32_t cf = 0;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int col = (int)(col0 + (int64_t)nt * col_step + ln);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t bit = 1u << (nt * 4 + q);
+                    if ((pending[mt] & bit) && ranks_before(acc[mt][nt][q], col, tq[q], iq[q])) cf |= bit;
+                }
+            }
+            uint32_t pend = 0;
+            if (__ballot(cf != 0) != 0) {
+                int slot[NT * 4];
+#pragma unroll
+                for (int b = 0; b < NT * 4; ++b) {
+                    slot[b] = kCap;
+                    if (cf & (1u << b)) slot[b] = atomicAdd(&t.ccnt[r0 + (b & 3)], 1);
+                }
+#pragma unroll
+                for (int b = 0; b < NT * 4; ++b) {
+                    if (cf & (1u << b)) {
+                        const int nt = b >> 2, q = b & 3, r = r0 + q;
+                        if (slot[b] < kCap) {
+                            t.cval[r * kCap + slot[b]] = acc[mt][nt][q];
+                            t.cidx[r * kCap + slot[b]] = (int)(col0 + (int64_t)nt * col_step + ln);
+                        } else {
+                            pend |= 1u << b;
                         }
                     }
                 }
             }
+            pending[mt] = pend;
         }
-        first = false;
         if (WG) __syncthreads(); else wave_sync();
         const int li = lane & 15;
         for (int r = q0 + (lane >> 4); r < n_merge_rows; r += q_step) {
@@ -458,6 +522,7 @@ __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t
         t.thr = reinterpret_cast<float*>(b + 16 * kTopK * 8 + 16 * kCap * 8);
         t.thri = reinterpret_cast<int*>(t.thr + 16);
         t.ccnt = t.thri + 16;
+        t.seed = nullptr;
         return t;
     };
     TopkRows tk = make_rows(wave);
@@ -535,7 +600,7 @@ struct WideCfg {
     static constexpr size_t LDS_BUF = TILE * (DBUF ? 2 : 1);
     static constexpr size_t LDS_LIST = (size_t)MB * kTopK * 8 + (size_t)MB * 12;
     static constexpr size_t LDS = LDS_BUF + LDS_LIST;
-    static_assert((size_t)MB * kCap * 8 <= LDS_BUF, "candidate buffers must fit in the chunk tile");
+    static_assert((size_t)MB * (kCap * 8 + 16 * 4) <= LDS_BUF, "candidate buffers and seeds must fit in the chunk tile");
     static_assert(NB % RPL == 0 && WLOADS > 0, "whole W loads");
     static_assert(LDS <= 160 * 1024, "LDS per workgroup");
 };
@@ -567,6 +632,7 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
     tk.ccnt = tk.thri + C::MB;
     tk.cval = reinterpret_cast<float*>(smem);  // aliases the chunk tile (epilogue only)
     tk.cidx = reinterpret_cast<int*>(smem + C::MB * kCap * 4);
+    tk.seed = reinterpret_cast<uint32_t*>(smem + C::MB * kCap * 8);  // also in the chunk tile
 
     // workgroup -> (M-block, slot): the M-blocks of one slot are dispatched
     // back to back on the same XCD so they share the slot's W rows in L2.
@@ -709,7 +775,7 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
             __syncthreads();
         }
         topk_epilogue<MW, NT, true>(acc, tk, wm * 16 * MW, m0 + wm * 16 * MW, M, col0 + wn * 16, 16 * WN,
-                                    nt_act, V, mw_act, rows_blk, wave * 4, 8 * WN);
+                                    nt_act, V, mw_act, rows_blk, wave * 4, 8 * WN, t0 == t_begin);
     }
 
     for (int e = tid; e < rows_blk * kTopK; e += C::THREADS) {
