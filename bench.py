@@ -2,9 +2,10 @@
 """Draft-verify cycles/s of the DFlash 2 cycle tail on one MI355X.
 
 One step = one cycle tail over one batch of synthetic inputs resident in HBM:
-five two-tap conv calls (one per drafter layer), the LM head with top-16, the
-pair selector, and verification (greedy, sampled, or half of each), each a
-C-ABI call on one stream.  Inputs rotate over enough copies to exceed the
+the two-tap conv over the five drafter layers' hidden states (one call: the
+layers' sequences are contiguous), the LM head with top-16, the pair
+selector, and verification (greedy, sampled, or half of each), each a C-ABI
+call on one stream.  Inputs rotate over enough copies to exceed the
 256 MB Infinity Cache, so every step streams its inputs from HBM.  The cycles
 are timed twice: launched eagerly (with per-stage events) and replayed from
 one captured HIP graph per input set (the reported value; the replayed outputs
@@ -78,7 +79,10 @@ class CycleRunner:
         B, T, P, L = cfg.B, cfg.T, cfg.P, cfg.L
         self.cfg = cfg
         self.torch = torch
-        self.y = [torch.empty_like(sets[0]["x"][l]) for l in range(L)]
+        # the L drafter layers' sequences are contiguous ([L][B][T][D]), so one
+        # conv call covers all of them (S = L * B sequences)
+        self.y_all = torch.empty_like(sets[0]["x"])
+        self.y = [self.y_all[l] for l in range(L)]
         self.tv = torch.empty((cfg.M, 16), dtype=torch.float32, device=dev)
         self.ti = torch.empty((cfg.M, 16), dtype=torch.int32, device=dev)
         self.rank = torch.empty((B, P), dtype=torch.int32, device=dev)
@@ -102,7 +106,7 @@ class CycleRunner:
         """The cycle's C-ABI calls on input set s, bound to the current stream."""
         dfl, cfg, B, L, g = self.dfl, self.cfg, self.cfg.B, self.cfg.L, self.g
         tv3, ti3 = self.tv.view(B, cfg.P, 16), self.ti.view(B, cfg.P, 16)
-        conv = [dfl.bind_conv2tap(s["x"][l], s["taps"][l], self.y[l]) for l in range(L)]
+        conv = [dfl.bind_conv2tap(s["x"], s["taps"], self.y_all)]
         head = dfl.bind_head_topk(s["h"], self.W, self.tv, self.ti, self.ws_head)
         sel = dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel)
         ver = []
@@ -342,7 +346,7 @@ def main():
                    "hidden": cfg.D, "vocab": cfg.V, "top_k": 16, "selector_rank": cfg.r,
                    "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets)},
         "roofline": head_roofline(cfg, head_us),
-        "stages_us": {"conv_x5": round(float(np.median(stage[:, 0])), 2),
+        "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),
                       "select_path": round(float(np.median(stage[:, 2])), 2),
                       "verify": round(float(np.median(stage[:, 3])), 2)},
