@@ -161,3 +161,121 @@ def _edge_margin(weights, target):
     lo = c[k - 1] if k > 0 else 0.0
     hi = c[k] if k < c.size else math.inf
     return min(abs(target - lo), abs(hi - target)) / total
+
+
+# ------------------------------------------------- top-k / top-p (nucleus)
+# Source: latenode.com "DFlash 2: un drafter de 3.43x...", FAQ (the published
+# figures sample at temperature 1.0 with top-p 0.95 and top-k 20).  The page
+# gives the parameters only; the readings below are the usual ones.
+
+def filtered_set(row, inv_tau, top_k, top_p):
+    """Tokens of one target row kept by top-k, then top-p, with their weights.
+
+    Readings taken:
+    * rank tokens by logit, descending, ties to the lower id; keep the first
+      top_k (all of them if top_k >= V);
+    * weights e(v) = exp((l_v - l_max) * inv_tau), float64; Zk = their sum
+      accumulated in rank order;
+    * nucleus: walk the kept tokens in rank order accumulating c; a token is
+      kept while the mass before it is below top_p * Zk (the first token is
+      always kept), i.e. the shortest rank prefix whose mass reaches
+      top_p * Zk;
+    * the filtered target is p'(v) = e(v) / Z' on the kept set, Z' = the
+      accumulated mass of the kept prefix.
+    Returns (ids ascending, their weights, Z')."""
+    row = np.asarray(row, dtype=np.float64)
+    V = row.size
+    k = min(int(top_k), V)
+    order = np.lexsort((np.arange(V), -row))[:k]
+    e = np.exp((row[order] - row[order[0]]) * inv_tau)
+    zk = 0.0
+    for x in e:
+        zk += float(x)
+    bound = float(top_p) * zk
+    kept, c = 0, 0.0
+    for x in e:
+        if kept > 0 and c >= bound:
+            break
+        c += float(x)
+        kept += 1
+    ids = order[:kept]
+    w = e[:kept]
+    by_id = np.argsort(ids, kind="stable")
+    return ids[by_id].astype(np.int64), w[by_id], c
+
+
+def _cut_margin(row, inv_tau, top_k, top_p):
+    """Smallest distance, relative to Zk, of a nucleus accumulation from its
+    top_p * Zk bound (a keep/drop decision that rounding could flip)."""
+    row = np.asarray(row, dtype=np.float64)
+    k = min(int(top_k), row.size)
+    order = np.lexsort((np.arange(row.size), -row))[:k]
+    e = np.exp((row[order] - row[order[0]]) * inv_tau)
+    zk = float(np.sum(e))
+    c = np.cumsum(e)[:-1]
+    return float(np.min(np.abs(c - top_p * zk)) / zk) if c.size else math.inf
+
+
+def decide_slot_filtered(ids, w, Z, d, u_acc, u_res):
+    """decide_slot on the filtered target: a draft outside the kept set has
+    p'(d) = 0 and is rejected; the residual max(0, p' - onehot(d)) is p' with
+    d removed, drawn by inverse CDF over the kept ids in ascending order."""
+    j = int(np.searchsorted(ids, d))
+    inside = j < ids.size and ids[j] == d
+    ed = float(w[j]) if inside else 0.0
+    if u_acc * Z < ed:
+        return True, int(d)
+    resid = w.copy()
+    if inside:
+        resid[j] = 0.0
+    return False, int(ids[inverse_cdf(resid, u_res * (Z - ed))])
+
+
+def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0,
+                        return_margins=False):
+    """verify_sample with the target rows filtered by top-k then top-p
+    (``filtered_set``); decisions, uniforms and outputs as in verify_sample,
+    the bonus drawn from the filtered last row.  top_p is taken as float32,
+    like the temperature."""
+    L = f64(logits)
+    d = i64(draft)
+    rid = i64(request_id)
+    p0 = i64(pos0)
+    B, T, V = L.shape
+    P = T - 1
+    inv_tau = 1.0 / float(np.float32(temperature))
+    tp = float(np.float32(top_p))
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_emit = np.zeros(B, dtype=np.int32)
+    margins = np.full(B, np.inf)
+    for b in range(B):
+        n = 0
+        for s in range(1, T + 1):
+            u_acc, u_res = uniforms(int(seed), int(rid[b]), int(p0[b]) + s)
+            t = s - 1 if s <= P else T - 1
+            ids, w, Z = filtered_set(L[b, t], inv_tau, top_k, tp)
+            if return_margins:
+                margins[b] = min(margins[b], _cut_margin(L[b, t], inv_tau, top_k, tp))
+            if s <= P:
+                tok = int(d[b, s - 1])
+                if return_margins:
+                    j = int(np.searchsorted(ids, tok))
+                    ed = float(w[j]) if j < ids.size and ids[j] == tok else 0.0
+                    margins[b] = min(margins[b], abs(u_acc * Z - ed) / Z)
+                    resid = w.copy()
+                    if ed > 0:
+                        resid[j] = 0.0
+                    margins[b] = min(margins[b], _edge_margin(resid, u_res * (Z - ed)))
+                accepted, tok = decide_slot_filtered(ids, w, Z, tok, u_acc, u_res)
+                out[b, n] = tok
+                if accepted:
+                    n += 1
+                    continue
+                break
+            if return_margins:
+                margins[b] = min(margins[b], _edge_margin(w, u_res * Z))
+            out[b, n] = int(ids[inverse_cdf(w, u_res * Z)])
+        n_emit[b] = n + 1
+    if return_margins:
+        return out, n_emit, margins
+    return out, n_emit

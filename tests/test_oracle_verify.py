@@ -172,3 +172,123 @@ def test_chi_square_bonus_token_after_full_accept():
     out, n = verify_sample(L, np.full((N, 1), 4), 1.0, 17, np.arange(N), np.zeros(N, np.int64))
     assert np.all(n == 2) and np.all(out[:, 0] == 4)
     assert chi2_pvalue(out[:, 1], p_of(row1), N) > 1e-3
+
+
+# ------------------------------------------------- top-k / top-p sampling
+from oracle.verify import filtered_set, verify_sample_topkp  # noqa: E402
+
+
+def _greedyish(seed, B=24, T=8, V=40):
+    rng = np.random.default_rng(seed)
+    L = rng.standard_normal((B, T, V)) * 2.0
+    g = np.argmax(L, -1)
+    d = g[:, :T - 1].copy()
+    cut = rng.integers(0, T, B)
+    for b in range(B):
+        if cut[b] < T - 1:
+            d[b, cut[b]] = (g[b, cut[b]] + 1) % V
+    return L, d, rng
+
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 0.95), (1, 1.0), (40, 1e-9), (7, 1e-30)])
+def test_topkp_single_token_is_greedy(top_k, top_p):
+    """Keeping one token makes p' one-hot at the argmax: every draft equal to
+    the argmax is accepted, any other rejected and replaced by the argmax,
+    and the bonus is the argmax, for any uniforms: exactly verify_greedy."""
+    L, d, rng = _greedyish(11)
+    for seed in (0, 5, 77):
+        rid = rng.integers(0, 2**40, L.shape[0])
+        o, n = verify_sample_topkp(L, d, 1.0, top_k, top_p, seed, rid, rng.integers(0, 2**30, L.shape[0]))
+        o0, n0 = verify_greedy(L, d)
+        assert np.array_equal(o, o0) and np.array_equal(n, n0)
+
+
+def test_topkp_worked_nucleus():
+    """p = (0.5, 0.3, 0.15, 0.05) on shuffled ids: top-p 0.9 keeps the three
+    largest (0.5 + 0.3 < 0.9 <= 0.95); 0.45 keeps one, 0.55 two; top-k 2
+    caps at two; weights stay proportional to p."""
+    ids = np.array([7, 2, 9, 4])
+    row = np.full(12, -np.inf)
+    row[ids] = np.log([0.5, 0.3, 0.15, 0.05])
+    row[np.isinf(row)] = -50.0
+    for top_k, top_p, kept in [(20, 0.9, [7, 2, 9]), (20, 0.45, [7]), (20, 0.55, [7, 2]),
+                               (2, 0.99, [7, 2]), (3, 1.0, [7, 2, 9])]:
+        got, w, Z = filtered_set(row, 1.0, top_k, top_p)
+        assert list(got) == sorted(kept)
+        p = {7: 0.5, 2: 0.3, 9: 0.15}
+        ref = np.array([p[i] for i in got])
+        assert np.allclose(w / Z, ref / ref.sum(), rtol=1e-12)
+
+
+def test_topkp_ties_at_the_k_boundary_keep_lower_ids():
+    row = np.array([1.0, 3.0, 3.0, 3.0, 0.0, 3.0])
+    got, w, Z = filtered_set(row, 1.0, 2, 1.0)
+    assert list(got) == [1, 2] and np.allclose(w, 1.0) and Z == 2.0
+
+
+def test_topkp_kept_set_is_the_shortest_ranked_prefix():
+    """Invariant on random rows: the kept tokens are the best-ranked ones, the
+    mass before the last kept token is below top_p * Zk and the kept mass
+    reaches it (unless top-k ran out), and the weights are exp((l - max)/tau)."""
+    rng = np.random.default_rng(3)
+    for _ in range(200):
+        V = int(rng.integers(1, 300))
+        row = rng.standard_normal(V) * rng.uniform(0.1, 5.0)
+        tau = rng.uniform(0.3, 2.0)
+        k, tp = int(rng.integers(1, 70)), float(rng.uniform(0.05, 1.0))
+        ids, w, Z = filtered_set(row, 1.0 / tau, k, tp)
+        rank = np.lexsort((np.arange(V), -row))
+        assert set(ids) == set(rank[:ids.size])
+        e_all = np.exp((row[rank[:min(k, V)]] - row.max()) / tau)
+        zk, cum = e_all.sum(), np.cumsum(e_all)
+        n = ids.size
+        assert n == 1 or cum[n - 2] < tp * zk * (1 + 1e-12)
+        assert n == min(k, V) or cum[n - 1] >= tp * zk * (1 - 1e-12)
+        assert np.allclose(w, np.exp((row[ids] - row.max()) / tau), rtol=1e-12)
+        assert np.isclose(Z, w.sum(), rtol=1e-12)
+
+
+def test_topkp_chi_square_first_token_follows_filtered_target():
+    """Over many Philox counters, the first emitted token follows p'
+    (top-20, top-p 0.8), for a draft inside the kept set and one outside."""
+    rng = np.random.default_rng(21)
+    V, N = 60, 40000
+    row = rng.standard_normal(V) * 1.5
+    ids, w, Z = filtered_set(row, 1.0, 20, 0.8)
+    p = np.zeros(V)
+    p[ids] = w / Z
+    outside = int(np.setdiff1d(np.arange(V), ids)[0])
+    for d0 in (int(ids[np.argsort(-w)[1]]), outside):
+        L = np.broadcast_to(np.stack([row, rng.standard_normal(V)])[None], (N, 2, V))
+        o, _ = verify_sample_topkp(L, np.full((N, 1), d0), 1.0, 20, 0.8, 4, np.arange(N), np.full(N, 9))
+        obs = np.bincount(o[:, 0], minlength=V)
+        assert obs[p == 0].sum() == 0
+        keep = p > 0
+        chi = stats.chisquare(obs[keep], N * p[keep])
+        assert chi.pvalue > 1e-3, chi
+
+
+def test_topkp_chi_square_bonus_follows_filtered_last_row():
+    """A draft with overwhelming weight is always accepted (T = 2), so the
+    bonus is drawn from the filtered last row."""
+    rng = np.random.default_rng(22)
+    V, N = 50, 30000
+    r0 = rng.standard_normal(V)
+    r0[13] = 60.0
+    r1 = rng.standard_normal(V) * 2.0
+    L = np.broadcast_to(np.stack([r0, r1])[None], (N, 2, V))
+    o, n = verify_sample_topkp(L, np.full((N, 1), 13), 1.0, 10, 0.9, 8, np.arange(N), np.zeros(N))
+    assert np.all(n == 2) and np.all(o[:, 0] == 13)
+    ids, w, Z = filtered_set(r1, 1.0, 10, 0.9)
+    obs = np.bincount(o[:, 1], minlength=V)
+    assert obs[np.setdiff1d(np.arange(V), ids)].sum() == 0
+    chi = stats.chisquare(obs[ids], N * w / Z)
+    assert chi.pvalue > 1e-3, chi
+
+
+def test_topkp_unfiltered_limit_keeps_every_weighted_token():
+    rng = np.random.default_rng(23)
+    row = rng.standard_normal(500) * 3.0
+    ids, w, Z = filtered_set(row, 1.0, 10**9, 1.0)
+    assert np.array_equal(ids, np.arange(500))
+    assert np.allclose(w, row_weights(row, 1.0), rtol=1e-15)
