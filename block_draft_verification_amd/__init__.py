@@ -34,6 +34,8 @@ _SIGNATURES = {
     "dflash_verify_greedy": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _p, _p, _p, _psz, _p]),
     "dflash_verify_sample": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p, _p,
                                             _p, _p, _p, _psz, _p]),
+    "dflash_verify_sample_topkp": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_f32,
+                                                  _c_u64, _p, _p, _p, _p, _p, _psz, _p]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -207,6 +209,33 @@ def verify_sample(logits, draft, temperature, seed, request_id, pos0, workspace=
     return o, n
 
 
+def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0, workspace=None,
+                        out=None):
+    """Rejection-sampling verification against the top-k, then top-p
+    filtered target; arguments as for verify_sample plus top_k (1..64) and
+    top_p (0, 1]."""
+    _need(logits, torch.float32, "logits", 3)
+    _need(draft, torch.int32, "draft", 2)
+    _need(request_id, torch.int64, "request_id", 1)
+    _need(pos0, torch.int64, "pos0", 1)
+    B, T, V = logits.shape
+    if tuple(draft.shape) != (B, T - 1) or request_id.numel() != B or pos0.numel() != B:
+        raise DFlashError("shape mismatch in verify_sample_topkp")
+    if out is None:
+        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
+        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    else:
+        o, n = out
+    L = lib()
+    before = (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(top_k), float(top_p),
+              int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
+    ws, nbytes = _workspace(L.dflash_verify_sample_topkp, before, (_stream(logits.device),), logits.device,
+                            workspace)
+    _check(L.dflash_verify_sample_topkp(*before, _ptr(ws), ctypes.byref(nbytes), _stream(logits.device)),
+           "dflash_verify_sample_topkp")
+    return o, n
+
+
 # --------------------------------------------------------------------------
 # Pre-marshalled calls for tight loops: each bind_* checks its tensors once and
 # returns a zero-argument callable that makes exactly one C-ABI call on the
@@ -268,10 +297,20 @@ def bind_verify_sample(logits, draft, temperature, seed, request_id, pos0, out_t
                    ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_sample")
 
 
+def bind_verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0, out_tok, n_emit,
+                             workspace):
+    B, T, V = logits.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_verify_sample_topkp,
+                  (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(top_k), float(top_p),
+                   int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(out_tok), _ptr(n_emit),
+                   _ptr(workspace), ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_sample_topkp")
+
+
 def workspace_bytes(op, *shape_args):
     """Workspace size of an entry point for the given sizes, without a GPU call:
     op in {"head_topk": (M, D, V), "select_path": (B, P), "verify_greedy": (B, T, V),
-    "verify_sample": (B, T, V)}."""
+    "verify_sample": (B, T, V), "verify_sample_topkp": (B, T, V, top_k)}."""
     L = lib()
     n = ctypes.c_size_t(0)
     fake = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
@@ -289,6 +328,10 @@ def workspace_bytes(op, *shape_args):
         B, T, V = shape_args
         code = L.dflash_verify_sample(fake[0], fake[1], B, T, V, 1.0, 0, fake[4], fake[5], fake[2], fake[3],
                                       None, ctypes.byref(n), None)
+    elif op == "verify_sample_topkp":
+        B, T, V, k = shape_args
+        code = L.dflash_verify_sample_topkp(fake[0], fake[1], B, T, V, 1.0, k, 1.0, 0, fake[4], fake[5], fake[2],
+                                            fake[3], None, ctypes.byref(n), None)
     else:
         raise ValueError(op)
     _check(code, f"workspace query {op}")

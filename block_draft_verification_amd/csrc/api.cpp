@@ -20,10 +20,13 @@ int launch_select_path(const float*, const int32_t*, const float*, const float*,
 size_t select_workspace_bytes(int B, int P);
 size_t greedy_workspace_bytes(int B, int T, int64_t V);
 size_t sample_workspace_bytes(int B, int T, int64_t V);
+size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k);
 int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
                          hipStream_t);
 int launch_verify_sample(const float*, const int32_t*, int, int, int64_t, float, uint64_t, const uint64_t*,
                          const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
+int launch_verify_sample_topkp(const float*, const int32_t*, int, int, int64_t, float, int, float, uint64_t,
+                               const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 }  // namespace dflash
 
 using namespace dflash;
@@ -219,6 +222,34 @@ int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B, i
     if (st != DFLASH_OK) return st;
     return launch_verify_sample(logits, draft, B, T, V, temperature, seed, request_id, pos0, out_tok, n_emit,
                                 workspace, (hipStream_t)stream);
+}
+
+int dflash_verify_sample_topkp(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
+                               float temperature, int32_t top_k, float top_p, uint64_t seed,
+                               const uint64_t* request_id, const int64_t* pos0, int32_t* out_tok,
+                               int32_t* n_emit, void* workspace, size_t* workspace_bytes, void* stream) {
+    int st = verify_common_checks(logits, draft, B, T, V, out_tok, n_emit);
+    if (st != DFLASH_OK) return st;
+    if (!request_id || !pos0 || !(temperature > 0.0f) || !isfinite(temperature)) return DFLASH_ERR_INVALID;
+    if (top_k < 1 || top_k > 64 || !(top_p > 0.0f) || !(top_p <= 1.0f)) return DFLASH_ERR_INVALID;
+    if (((uintptr_t)request_id & 7u) || ((uintptr_t)pos0 & 7u)) return DFLASH_ERR_INVALID;
+    const size_t no = (size_t)B * T * 4, nn = (size_t)B * 4, n8 = (size_t)B * 8;
+    if (overlap(out_tok, no, request_id, n8) || overlap(out_tok, no, pos0, n8) ||
+        overlap(n_emit, nn, request_id, n8) || overlap(n_emit, nn, pos0, n8))
+        return DFLASH_ERR_INVALID;
+    bool query = false;
+    st = workspace_check(workspace, workspace_bytes, sample_topkp_workspace_bytes(B, T, V, top_k), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    if (overlap(workspace, nws, logits, (size_t)B * T * V * 4) ||
+        overlap(workspace, nws, draft, (size_t)B * (T - 1) * 4) || overlap(workspace, nws, out_tok, no) ||
+        overlap(workspace, nws, n_emit, nn) || overlap(workspace, nws, request_id, n8) ||
+        overlap(workspace, nws, pos0, n8))
+        return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_verify_sample_topkp(logits, draft, B, T, V, temperature, top_k, top_p, seed, request_id, pos0,
+                                      out_tok, n_emit, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

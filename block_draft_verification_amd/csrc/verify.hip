@@ -17,6 +17,7 @@
 // decisions agree with an exact evaluation except within ~1e-15 of a boundary.
 
 #include "common.hpp"
+#include "keysort.hpp"
 
 namespace dflash {
 
@@ -429,6 +430,320 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
     }
 }
 
+// ================================================ top-k / top-p sampling
+// Source: latenode.com "DFlash 2: un drafter de 3.43x...", FAQ (the published
+// figures sample at temperature 1.0, top-p 0.95, top-k 20).  The target row is
+// filtered before the rejection test: its top_k logits (ties to the lower id),
+// weights exp((l - l_max) / tau), then the shortest rank prefix whose mass
+// reaches top_p of theirs; the decisions are those of the unfiltered sampler
+// on the filtered distribution.
+//
+// topk_chunk_kernel streams the logits once (the same 4096-entry chunks) and
+// writes each chunk's top_k keys (rank_key, descending).  Threshold first:
+// each wavefront sorts its 64 lanes' best keys, the top_k-th of them is
+// reached by top_k distinct entries, and the largest such bound over the
+// wavefronts leaves only a few dozen candidates, which one wavefront sorts.
+// topkp_decide_kernel (one workgroup per request) merges a row's chunk lists
+// the same way, evaluates the nucleus in float64 in rank order, sorts the
+// kept tokens by id and takes the slot decisions.
+constexpr int kMaxTopK = 64;
+constexpr int kCandCap = kVerifyThreads;  // candidates sorted per chunk or row
+
+// Top 64 of two descending 64-key sequences a (this lane: a[lane]) and b:
+// the lane-wise maximum with b reversed is bitonic; half-cleaners sort it.
+__device__ __forceinline__ uint64_t merge64_desc(uint64_t a, uint64_t b_rev, int lane) {
+    uint64_t k = a > b_rev ? a : b_rev;
+    k = cx(k, xor_lane_u64<32>(k, lane), (lane & 32) == 0);
+    k = cx(k, xor_lane_u64<16>(k, lane), (lane & 16) == 0);
+    k = cx(k, xor_lane_u64<8>(k, lane), (lane & 8) == 0);
+    k = cx(k, xor_lane_u64<4>(k, lane), (lane & 4) == 0);
+    k = cx(k, xor_lane_u64<2>(k, lane), (lane & 2) == 0);
+    k = cx(k, xor_lane_u64<1>(k, lane), (lane & 1) == 0);
+    return k;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Appends this lane's keys >= thr (and non-zero) to cand[] at a workgroup
+// counter; returns nothing, the count is *count (may exceed kCandCap: then
+// only the first kCandCap are stored).
+template <int N>
+__device__ __forceinline__ void gather_candidates(const uint64_t (&k)[N], uint64_t thr, uint64_t* cand,
+                                                  int* count) {
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) mine += (k[i] != 0 && k[i] >= thr) ? 1 : 0;
+    // wavefront exclusive prefix of the counts, then one reservation per wavefront
+    const int lane = threadIdx.x & 63;
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    const int total = __shfl(incl, 63);
+    int base = 0;
+    if (lane == 63 && total > 0) base = atomicAdd(count, total);
+    base = __shfl(base, 63) + incl - mine;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        if (k[i] != 0 && k[i] >= thr) {
+            if (base < kCandCap) cand[base] = k[i];
+            ++base;
+        }
+}
+
+// The best `keep` (<= 64) of n <= kCandCap candidate keys in cand[], sorted
+// descending, in lanes 0..keep-1 of wavefront 0 (other lanes: 0).  All
+// threads of the workgroup call it; grp[] is LDS scratch of kCandCap keys.
+__device__ __forceinline__ uint64_t best_of_candidates(const uint64_t* cand, int n, uint64_t* grp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint64_t k = (threadIdx.x < n) ? cand[threadIdx.x] : 0ull;
+    if (n > 64) {
+        k = sort64_desc(k, lane);
+        grp[threadIdx.x] = k;
+        __syncthreads();
+        if (wave == 0) {
+            const uint64_t a = merge64_desc(grp[lane], grp[64 + 63 - lane], lane);
+            const uint64_t b = merge64_desc(grp[128 + lane], grp[192 + 63 - lane], lane);
+            k = merge64_desc(a, __shfl(b, 63 - lane), lane);
+        }
+        __syncthreads();
+    } else if (wave == 0) {
+        k = sort64_desc(k, lane);
+    }
+    return k;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kVerifyThreads) void topk_chunk_kernel(const float* __restrict__ logits, int64_t V,
+                                                                    int n_chunks, int top_k,
+                                                                    uint64_t* __restrict__ part) {
+    __shared__ uint64_t s_thr[4];
+    __shared__ uint64_t cand[kCandCap];
+    __shared__ uint64_t grp[kCandCap];
+    __shared__ int s_count;
+    const int64_t row = blockIdx.y;
+    const int chunk = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float v[kPerThread];
+    int idx[kPerThread];
+    load_chunk<VEC>(logits + row * V, V, chunk, v, idx);
+    uint64_t k[kPerThread];
+    uint64_t mk = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+        k[i] = idx[i] != 0x7FFFFFFF ? rank_key(v[i], idx[i]) : 0ull;
+        mk = k[i] > mk ? k[i] : mk;
+    }
+    if (threadIdx.x == 0) s_count = 0;
+    // the wavefront's top_k-th best lane maximum: top_k distinct entries reach it
+    const uint64_t sorted = sort64_desc(mk, lane);
+    if (lane == 0) s_thr[wave] = readlane_u64(sorted, top_k - 1);
+    __syncthreads();
+    uint64_t thr = s_thr[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) thr = s_thr[w] > thr ? s_thr[w] : thr;
+    gather_candidates(k, thr, cand, &s_count);
+    __syncthreads();
+    const int n = s_count;
+    uint64_t* out = part + ((int64_t)row * n_chunks + chunk) * top_k;
+    if (n <= kCandCap) {
+        const uint64_t best = best_of_candidates(cand, n, grp);
+        if (wave == 0 && lane < top_k) out[lane] = best;
+        return;
+    }
+    // more than kCandCap entries tie at the bound (e.g. constant rows): take
+    // the best top_k one at a time
+    __shared__ uint64_t s_best[4];
+    for (int r = 0; r < top_k; ++r) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i) m = k[i] > m ? k[i] : m;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = shfl_xor_u64(m, off);
+            m = o > m ? o : m;
+        }
+        if (lane == 0) s_best[wave] = m;
+        __syncthreads();
+        uint64_t b = s_best[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) b = s_best[w] > b ? s_best[w] : b;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kPerThread; ++i)
+            if (k[i] == b) k[i] = 0;  // keys are unique (distinct ids)
+        if (threadIdx.x == 0) out[r] = b;
+    }
+}
+
+__global__ __launch_bounds__(kVerifyThreads) void topkp_decide_kernel(
+    const int32_t* __restrict__ draft, const uint64_t* __restrict__ part,
+    int T, int64_t V, int n_chunks, int top_k, double inv_tau, double top_p, uint64_t seed,
+    const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0, int32_t* __restrict__ out_tok,
+    int32_t* __restrict__ n_emit) {
+    __shared__ uint64_t cand[kCandCap];
+    __shared__ uint64_t grp[kCandCap];
+    __shared__ int s_count;
+    __shared__ uint64_t s_thr;
+    __shared__ double s_e[kMaxTopK];
+    __shared__ int s_id[kMaxTopK];
+    __shared__ int kept_id[16][kMaxTopK];   // per row: kept ids ascending
+    __shared__ double kept_w[16][kMaxTopK];  // and their weights
+    __shared__ int kept_n[16];
+    __shared__ double kept_z[16];
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // ---- per row: the filtered set
+    for (int t = 0; t < T; ++t) {
+        const uint64_t* lists = part + ((int64_t)b * T + t) * n_chunks * top_k;
+        // bound: the top_k-th best list head (a running top 64 over groups of heads)
+        if (wave == 0) {
+            uint64_t run = 0;
+            for (int g = 0; g < n_chunks; g += 64) {
+                uint64_t h = (g + lane < n_chunks) ? lists[(int64_t)(g + lane) * top_k] : 0ull;
+                h = sort64_desc(h, lane);
+                run = g == 0 ? h : merge64_desc(run, __shfl(h, 63 - lane), lane);
+            }
+            const uint64_t thr = readlane_u64(run, top_k - 1);
+            if (lane == 0) {
+                s_thr = thr;
+                s_count = 0;
+            }
+        }
+        __syncthreads();
+        const uint64_t thr = s_thr;
+        // candidates: the entries at or above the bound (a prefix of each list)
+        for (int c = threadIdx.x; c < n_chunks; c += kVerifyThreads) {
+            for (int j = 0; j < top_k; ++j) {
+                const uint64_t key = lists[(int64_t)c * top_k + j];
+                if (key == 0 || key < thr) break;
+                const int pos = atomicAdd(&s_count, 1);
+                if (pos < kCandCap) cand[pos] = key;
+            }
+        }
+        __syncthreads();
+        const int n = s_count;
+        uint64_t best;
+        if (n <= kCandCap) {
+            best = best_of_candidates(cand, n, grp);
+        } else {
+            // ties beyond the buffer: k-way selection of the best top_k heads
+            best = 0;
+            if (wave == 0) {
+                for (int r = 0; r < top_k; ++r) {
+                    uint64_t m = 0;
+                    for (int c = lane; c < n_chunks; c += 64)
+                        for (int j = 0; j < top_k; ++j) {
+                            const uint64_t key = lists[(int64_t)c * top_k + j];
+                            const bool taken = r > 0 && key >= readlane_u64(best, r - 1);
+                            if (!taken && key > m) m = key;
+                            if (!taken) break;
+                        }
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) {
+                        const uint64_t o = shfl_xor_u64(m, off);
+                        m = o > m ? o : m;
+                    }
+                    if (lane == r) best = m;
+                }
+            }
+        }
+        // weights in rank order, then the nucleus in float64, sequentially
+        if (wave == 0) {
+            const bool real = lane < top_k && best != 0;
+            const double lv = real ? (double)key_value(best) : 0.0;
+            const double l0 = (double)key_value(readlane_u64(best, 0));
+            s_e[lane] = real ? exp((lv - l0) * inv_tau) : 0.0;
+            s_id[lane] = real ? key_id(best) : 0x7FFFFFFF;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double zk = 0.0;
+            int nk = 0;
+            for (int j = 0; j < top_k && s_id[j] != 0x7FFFFFFF; ++j) {
+                zk += s_e[j];
+                ++nk;
+            }
+            const double bound = top_p * zk;
+            double c = 0.0;
+            int kept = 0;
+            for (int j = 0; j < nk; ++j) {
+                if (kept > 0 && c >= bound) break;
+                c += s_e[j];
+                ++kept;
+            }
+            kept_n[t] = kept;
+            kept_z[t] = c;
+        }
+        __syncthreads();
+        // kept tokens by ascending id
+        if (wave == 0) {
+            const int kept = kept_n[t];
+            uint64_t ik = lane < kept ? (((uint64_t)(0x7FFFFFFF - s_id[lane]) << 32) | (uint32_t)lane) : 0ull;
+            ik = sort64_desc(ik, lane);
+            if (lane < kept) {
+                const int j = (int)(uint32_t)ik;
+                kept_id[t][lane] = s_id[j];
+                kept_w[t][lane] = s_e[j];
+            }
+        }
+        __syncthreads();
+    }
+    // ---- decisions, in slot order (one thread; at most 64 kept tokens a row)
+    if (threadIdx.x == 0) {
+        const int P = T - 1;
+        const uint64_t rid = request_id[b];
+        const int64_t p0 = pos0[b];
+        int32_t* o = out_tok + (int64_t)b * T;
+        int n = 0, emitted = -1;
+        for (int s = 1; s <= T && emitted < 0; ++s) {
+            const int t = (s <= P) ? s - 1 : T - 1;
+            const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
+            const double u_acc = (double)(r.w[0] >> 11) * 0x1p-53, u_res = (double)(r.w[1] >> 11) * 0x1p-53;
+            const int kept = kept_n[t];
+            const double Z = kept_z[t];
+            int skip = -1;
+            double ed = 0.0;
+            if (s <= P) {
+                const int d = draft[(int64_t)b * P + (s - 1)];
+                for (int i = 0; i < kept; ++i)
+                    if (kept_id[t][i] == d) {
+                        skip = i;
+                        ed = kept_w[t][i];
+                    }
+                if (u_acc * Z < ed) {
+                    o[n++] = d;
+                    continue;
+                }
+            }
+            const double target = u_res * (Z - ed);
+            double run = 0.0;
+            int last = -1;
+            for (int i = 0; i < kept; ++i) {
+                const double w = i == skip ? 0.0 : kept_w[t][i];
+                run += w;
+                if (w > 0.0) {
+                    last = i;
+                    if (run > target) {
+                        emitted = kept_id[t][i];
+                        break;
+                    }
+                }
+            }
+            if (emitted < 0) emitted = last >= 0 ? kept_id[t][last] : kept_id[t][0];
+        }
+        o[n] = emitted;
+        for (int k = n + 1; k < T; ++k) o[k] = -1;
+        n_emit[b] = n + 1;
+    }
+}
+
 // ------------------------------------------------------------------- hosts
 size_t greedy_workspace_bytes(int B, int T, int64_t V) {
     const int64_t n_chunks = (V + kChunk - 1) / kChunk;
@@ -474,6 +789,34 @@ int launch_verify_sample(const float* logits, const int32_t* draft, int B, int T
     if (st != DFLASH_OK) return st;
     hipLaunchKernelGGL(sample_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, logits, draft, stats, T, V,
                        n_chunks, inv_tau, seed, request_id, pos0, out_tok, n_emit);
+    return launch_status();
+}
+
+size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k) {
+    const int64_t n_chunks = (V + kChunk - 1) / kChunk;
+    return (size_t)B * T * n_chunks * top_k * sizeof(uint64_t);
+}
+
+int launch_verify_sample_topkp(const float* logits, const int32_t* draft, int B, int T, int64_t V,
+                               float temperature, int top_k, float top_p, uint64_t seed,
+                               const uint64_t* request_id, const int64_t* pos0, int32_t* out_tok,
+                               int32_t* n_emit, void* ws, hipStream_t stream) {
+    if (top_k < 1 || top_k > kMaxTopK || T > 16) return DFLASH_ERR_INVALID;  // the ABI bounds, again
+    const int n_chunks = (int)((V + kChunk - 1) / kChunk);
+    uint64_t* part = reinterpret_cast<uint64_t*>(ws);
+    const double inv_tau = 1.0 / (double)temperature;
+    const dim3 grid(n_chunks, B * T);
+    const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL(topk_chunk_kernel<true>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks,
+                           top_k, part);
+    else
+        hipLaunchKernelGGL(topk_chunk_kernel<false>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks,
+                           top_k, part);
+    int st = launch_status();
+    if (st != DFLASH_OK) return st;
+    hipLaunchKernelGGL(topkp_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, draft, part, T, V,
+                       n_chunks, top_k, inv_tau, (double)top_p, seed, request_id, pos0, out_tok, n_emit);
     return launch_status();
 }
 

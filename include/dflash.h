@@ -10,6 +10,11 @@
  *   dflash_verify_greedy  greedy longest-prefix acceptance
  *   dflash_verify_sample  rejection-sampling acceptance (Philox4x64-10 draws)
  *
+ * and one variant of the last step:
+ *
+ *   dflash_verify_sample_topkp  rejection sampling against a top-k / top-p
+ *                               filtered target
+ *
  * Sources (the pages describe the method in words only):
  *   tamsi.dev, "DFlash 2 - 3x plus de tokens sur Qwen3.8-27B, meme sortie",
  *     section "L'idee, sans le papier" (top-16 lists, pair selector, two-tap
@@ -181,6 +186,33 @@ int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B,
                          const uint64_t* request_id, const int64_t* pos0,
                          int32_t* out_tok, int32_t* n_emit,
                          void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification against a filtered target.
+ * Source: latenode.com "DFlash 2: un drafter de 3.43x...", FAQ (the published
+ * figures sample at temperature 1.0 with top-p 0.95 and top-k 20).
+ * Each target row t is filtered before the test: rank tokens by logit,
+ * descending, ties to the lower id, and keep the first top_k; weights
+ * e(v) = exp((l_t(v) - max_v l_t) * (1/tau)) in float64; Zk = their sum in rank
+ * order; keep, in rank order, every token whose preceding mass is below
+ * top_p * Zk (the first always), giving the set N_t with mass Z'_t.  Then as
+ * dflash_verify_sample with p'_t = e / Z'_t on N_t (0 elsewhere): accept
+ * d = draft[b][s-1] iff d is in N_{s-1} and u_acc * Z' < e(d); on the first
+ * rejection emit the smallest id v in N with sum over ids w <= v in N, w != d,
+ * of e(w) > u_res * (Z' - e'(d)) (e'(d) = e(d) if d is in N, else 0) and stop;
+ * if every draft is accepted draw the bonus from N_{T-1} the same way with
+ * target u_res * Z'.  Uniforms as for dflash_verify_sample.
+ *   top_k   1..64 tokens kept per row before the nucleus cut
+ *   top_p   nucleus mass in (0, 1]
+ *   other arguments and outputs as for dflash_verify_sample.
+ * Requires B >= 1, 2 <= T <= 16, 1 <= V < 2^31, temperature finite and > 0,
+ * 1 <= top_k <= 64, 0 < top_p <= 1.  Logits must not be NaN.
+ */
+int dflash_verify_sample_topkp(const float* logits, const int32_t* draft, int32_t B,
+                               int32_t T, int64_t V, float temperature, int32_t top_k,
+                               float top_p, uint64_t seed, const uint64_t* request_id,
+                               const int64_t* pos0, int32_t* out_tok, int32_t* n_emit,
+                               void* workspace, size_t* workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -144,3 +144,23 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(dfl.DFlashError):
         dfl.conv2tap(x, torch.zeros(1, 8, 128, dtype=torch.bfloat16))
+
+
+@needs_lib
+def test_verify_topkp_validation():
+    f = dfl.lib().dflash_verify_sample_topkp
+    n = ctypes.c_size_t(0)
+    q = lambda B, T, V, tau, k, p: f(A[0], A[1], B, T, V, tau, k, p, 0, A[4], A[5], A[2], A[3], NULL,
+                                     ctypes.byref(n), NULL)
+    assert q(8, 8, 151936, 1.0, 20, 0.95) == OK and n.value == 8 * 8 * 38 * 20 * 8
+    for bad in [(8, 8, 100, 1.0, 0, 0.95), (8, 8, 100, 1.0, 65, 0.95), (8, 8, 100, 1.0, 20, 0.0),
+                (8, 8, 100, 1.0, 20, 1.5), (8, 8, 100, 1.0, 20, float("nan")), (8, 8, 100, 0.0, 20, 0.9),
+                (8, 17, 100, 1.0, 20, 0.9), (8, 1, 100, 1.0, 20, 0.9), (0, 8, 100, 1.0, 20, 0.9)]:
+        assert q(*bad) == INVALID, bad
+    small = ctypes.c_size_t(n.value - 1)
+    assert f(A[0], A[1], 8, 8, 151936, 1.0, 20, 0.95, 0, A[4], A[5], A[2], A[3], A[6], ctypes.byref(small),
+             NULL) == WORKSPACE
+    if not torch.cuda.is_available():
+        ok = ctypes.c_size_t(n.value)
+        assert f(A[0], A[1], 8, 8, 151936, 1.0, 20, 0.95, 0, A[4], A[5], A[2], A[3], A[6], ctypes.byref(ok),
+                 NULL) == DEVICE
