@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "head_topk_traffic.json")
-HEAD_SRC = os.path.join(ROOT, "block_draft_verification_amd", "csrc", "head_topk.hip")
+# the head kernels' sources: the kernel file and the key-sort header it includes
+HEAD_SRC = [os.path.join(ROOT, "block_draft_verification_amd", "csrc", f) for f in ("head_topk.hip", "keysort.hpp")]
 WORKLOAD_TEXT = {
     "c1_tiny": "batch 1, block 8, hidden 256, vocab 4096, top-16, selector rank 32, greedy",
     "c2_b1": "batch 1, block 8, hidden 5120, vocab 151936, top-16, selector rank 192, greedy",
@@ -52,6 +53,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="bound on the oracle's timed CPU work")
     ap.add_argument("--max-sets", type=int, default=64)
+    ap.add_argument("--sample-top-k", type=int, default=0,
+                    help="sampled requests: filter the target to its top-k, then top-p (0 = full softmax)")
+    ap.add_argument("--sample-top-p", type=float, default=1.0)
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -96,8 +100,12 @@ class CycleRunner:
         self.ws_head = torch.empty(dfl.workspace_bytes("head_topk", cfg.M, cfg.D, cfg.V), dtype=u8, device=dev)
         self.ws_sel = torch.empty(dfl.workspace_bytes("select_path", B, P), dtype=u8, device=dev)
         self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
-        self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
-                                device=dev)
+        if cfg.top_k > 0:
+            self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_topkp", max(B - g, 1), T, cfg.V, cfg.top_k),
+                                    dtype=u8, device=dev)
+        else:
+            self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
+                                    device=dev)
         self.F_l, self.F_r, self.W = F_l, F_r, W
         self.sets = sets
         self.calls = [self.bind_set(s) for s in sets]
@@ -113,8 +121,13 @@ class CycleRunner:
         if g > 0:
             ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
         if g < B:
-            ver.append(dfl.bind_verify_sample(s["target_s"], self.tok[g:], cfg.temperature, cfg.seed,
-                                              s["rid_s"], s["pos_s"], self.out[g:], self.n[g:], self.ws_s))
+            if cfg.top_k > 0:
+                ver.append(dfl.bind_verify_sample_topkp(s["target_s"], self.tok[g:], cfg.temperature, cfg.top_k,
+                                                        cfg.top_p, cfg.seed, s["rid_s"], s["pos_s"], self.out[g:],
+                                                        self.n[g:], self.ws_s))
+            else:
+                ver.append(dfl.bind_verify_sample(s["target_s"], self.tok[g:], cfg.temperature, cfg.seed,
+                                                  s["rid_s"], s["pos_s"], self.out[g:], self.n[g:], self.ws_s))
         return conv, head, sel, ver
 
     def capture(self):
@@ -200,8 +213,11 @@ def head_roofline(cfg, head_us):
 
 
 def head_source_sha():
-    with open(HEAD_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in HEAD_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(cfg):
@@ -226,12 +242,12 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
 
     host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     t0 = time.perf_counter()
-    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
+    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
     while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
-        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
+        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p)
         total += time.perf_counter() - t0
         n += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -268,7 +284,7 @@ def main():
 
     dfl.lib()
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config)
+    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p)
     log(f"[bench] config {cfg.name}: generating inputs on {dev}")
     inp = make_cycle_inputs(cfg, device=dev)
     sets, per_set = make_sets(torch, cfg, inp, args.max_sets)
@@ -344,7 +360,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT[cfg.name]}", "batch": cfg.B, "block": cfg.T,
                    "hidden": cfg.D, "vocab": cfg.V, "top_k": 16, "selector_rank": cfg.r,
-                   "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets)},
+                   "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets),
+                   **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {})},
         "roofline": head_roofline(cfg, head_us),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),

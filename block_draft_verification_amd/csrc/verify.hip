@@ -443,9 +443,10 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
 // each wavefront sorts its 64 lanes' best keys, the top_k-th of them is
 // reached by top_k distinct entries, and the largest such bound over the
 // wavefronts leaves only a few dozen candidates, which one wavefront sorts.
-// topkp_decide_kernel (one workgroup per request) merges a row's chunk lists
-// the same way, evaluates the nucleus in float64 in rank order, sorts the
-// kept tokens by id and takes the slot decisions.
+// topkp_set_kernel (one workgroup per row) merges the row's chunk lists the
+// same way, evaluates the nucleus in float64 in rank order and writes the
+// kept tokens by ascending id; topkp_decide_kernel (one per request) takes the
+// slot decisions from those records.
 constexpr int kMaxTopK = 64;
 constexpr int kCandCap = kVerifyThreads;  // candidates sorted per chunk or row
 
@@ -582,26 +583,30 @@ __global__ __launch_bounds__(kVerifyThreads) void topk_chunk_kernel(const float*
     }
 }
 
-__global__ __launch_bounds__(kVerifyThreads) void topkp_decide_kernel(
-    const int32_t* __restrict__ draft, const uint64_t* __restrict__ part,
-    int T, int64_t V, int n_chunks, int top_k, double inv_tau, double top_p, uint64_t seed,
-    const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0, int32_t* __restrict__ out_tok,
-    int32_t* __restrict__ n_emit) {
+// One target row's filtered set, written as a KeptSet record.
+struct KeptSet {
+    double z;                // Z': mass of the kept tokens
+    int n;                   // kept tokens (1..64)
+    int pad;
+    int id[kMaxTopK];        // ascending ids
+    double w[kMaxTopK];      // their weights exp((l - l_max) / tau)
+};
+
+__global__ __launch_bounds__(kVerifyThreads) void topkp_set_kernel(const uint64_t* __restrict__ part, int n_chunks,
+                                                                   int top_k, double inv_tau, double top_p,
+                                                                   KeptSet* __restrict__ sets) {
     __shared__ uint64_t cand[kCandCap];
     __shared__ uint64_t grp[kCandCap];
     __shared__ int s_count;
     __shared__ uint64_t s_thr;
     __shared__ double s_e[kMaxTopK];
     __shared__ int s_id[kMaxTopK];
-    __shared__ int kept_id[16][kMaxTopK];   // per row: kept ids ascending
-    __shared__ double kept_w[16][kMaxTopK];  // and their weights
-    __shared__ int kept_n[16];
-    __shared__ double kept_z[16];
-    const int b = blockIdx.x;
+    __shared__ int s_kept;
+    const int64_t row = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // ---- per row: the filtered set
-    for (int t = 0; t < T; ++t) {
-        const uint64_t* lists = part + ((int64_t)b * T + t) * n_chunks * top_k;
+    KeptSet* rec = sets + row;
+    {
+        const uint64_t* lists = part + row * n_chunks * top_k;
         // bound: the top_k-th best list head (a running top 64 over groups of heads)
         if (wave == 0) {
             uint64_t run = 0;
@@ -678,44 +683,87 @@ __global__ __launch_bounds__(kVerifyThreads) void topkp_decide_kernel(
                 c += s_e[j];
                 ++kept;
             }
-            kept_n[t] = kept;
-            kept_z[t] = c;
+            rec->n = kept;
+            rec->z = c;
+            s_kept = kept;
         }
         __syncthreads();
         // kept tokens by ascending id
         if (wave == 0) {
-            const int kept = kept_n[t];
+            const int kept = s_kept;
             uint64_t ik = lane < kept ? (((uint64_t)(0x7FFFFFFF - s_id[lane]) << 32) | (uint32_t)lane) : 0ull;
             ik = sort64_desc(ik, lane);
             if (lane < kept) {
                 const int j = (int)(uint32_t)ik;
-                kept_id[t][lane] = s_id[j];
-                kept_w[t][lane] = s_e[j];
+                rec->id[lane] = s_id[j];
+                rec->w[lane] = s_e[j];
             }
         }
         __syncthreads();
     }
+}
+
+__global__ __launch_bounds__(64) void topkp_decide_kernel(const int32_t* __restrict__ draft,
+                                                         const KeptSet* __restrict__ sets, int T, uint64_t seed,
+                                                         const uint64_t* __restrict__ request_id,
+                                                         const int64_t* __restrict__ pos0,
+                                                         int32_t* __restrict__ out_tok, int32_t* __restrict__ n_emit) {
+    __shared__ KeptSet s_sets[16];
+    __shared__ double s_u[16][2];
+    const int b = blockIdx.x;
+    // the request's records and every slot's uniforms, fetched and drawn in parallel
+    {
+        // lane l fetches entry l of every row: all loads in flight together
+        const KeptSet* src = sets + (int64_t)b * T;
+        const int l = threadIdx.x;
+        int id[16];
+        double w[16], z[16];
+        int n[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+            if (t < T) {
+                id[t] = src[t].id[l];
+                w[t] = src[t].w[l];
+                z[t] = src[t].z;
+                n[t] = src[t].n;
+            }
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+            if (t < T) {
+                s_sets[t].id[l] = id[t];
+                s_sets[t].w[l] = w[t];
+                if (l == 0) {
+                    s_sets[t].z = z[t];
+                    s_sets[t].n = n[t];
+                }
+            }
+        if (threadIdx.x < T) {
+            const int s = threadIdx.x + 1;
+            const Philox4 r = philox4x64_10(1ull, request_id[b], (uint64_t)(pos0[b] + s), 0ull, seed, 0ull);
+            s_u[threadIdx.x][0] = (double)(r.w[0] >> 11) * 0x1p-53;
+            s_u[threadIdx.x][1] = (double)(r.w[1] >> 11) * 0x1p-53;
+        }
+    }
+    __syncthreads();
     // ---- decisions, in slot order (one thread; at most 64 kept tokens a row)
     if (threadIdx.x == 0) {
         const int P = T - 1;
-        const uint64_t rid = request_id[b];
-        const int64_t p0 = pos0[b];
         int32_t* o = out_tok + (int64_t)b * T;
         int n = 0, emitted = -1;
         for (int s = 1; s <= T && emitted < 0; ++s) {
             const int t = (s <= P) ? s - 1 : T - 1;
-            const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
-            const double u_acc = (double)(r.w[0] >> 11) * 0x1p-53, u_res = (double)(r.w[1] >> 11) * 0x1p-53;
-            const int kept = kept_n[t];
-            const double Z = kept_z[t];
+            const double u_acc = s_u[s - 1][0], u_res = s_u[s - 1][1];
+            const KeptSet& ks = s_sets[t];
+            const int kept = ks.n;
+            const double Z = ks.z;
             int skip = -1;
             double ed = 0.0;
             if (s <= P) {
                 const int d = draft[(int64_t)b * P + (s - 1)];
                 for (int i = 0; i < kept; ++i)
-                    if (kept_id[t][i] == d) {
+                    if (ks.id[i] == d) {
                         skip = i;
-                        ed = kept_w[t][i];
+                        ed = ks.w[i];
                     }
                 if (u_acc * Z < ed) {
                     o[n++] = d;
@@ -726,17 +774,17 @@ __global__ __launch_bounds__(kVerifyThreads) void topkp_decide_kernel(
             double run = 0.0;
             int last = -1;
             for (int i = 0; i < kept; ++i) {
-                const double w = i == skip ? 0.0 : kept_w[t][i];
+                const double w = i == skip ? 0.0 : ks.w[i];
                 run += w;
                 if (w > 0.0) {
                     last = i;
                     if (run > target) {
-                        emitted = kept_id[t][i];
+                        emitted = ks.id[i];
                         break;
                     }
                 }
             }
-            if (emitted < 0) emitted = last >= 0 ? kept_id[t][last] : kept_id[t][0];
+            if (emitted < 0) emitted = last >= 0 ? ks.id[last] : ks.id[0];
         }
         o[n] = emitted;
         for (int k = n + 1; k < T; ++k) o[k] = -1;
@@ -794,7 +842,7 @@ int launch_verify_sample(const float* logits, const int32_t* draft, int B, int T
 
 size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k) {
     const int64_t n_chunks = (V + kChunk - 1) / kChunk;
-    return (size_t)B * T * n_chunks * top_k * sizeof(uint64_t);
+    return (size_t)B * T * n_chunks * top_k * sizeof(uint64_t) + (size_t)B * T * sizeof(KeptSet);
 }
 
 int launch_verify_sample_topkp(const float* logits, const int32_t* draft, int B, int T, int64_t V,
@@ -804,6 +852,7 @@ int launch_verify_sample_topkp(const float* logits, const int32_t* draft, int B,
     if (top_k < 1 || top_k > kMaxTopK || T > 16) return DFLASH_ERR_INVALID;  // the ABI bounds, again
     const int n_chunks = (int)((V + kChunk - 1) / kChunk);
     uint64_t* part = reinterpret_cast<uint64_t*>(ws);
+    KeptSet* sets = reinterpret_cast<KeptSet*>(part + (size_t)B * T * n_chunks * top_k);
     const double inv_tau = 1.0 / (double)temperature;
     const dim3 grid(n_chunks, B * T);
     const bool vec = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
@@ -815,8 +864,12 @@ int launch_verify_sample_topkp(const float* logits, const int32_t* draft, int B,
                            top_k, part);
     int st = launch_status();
     if (st != DFLASH_OK) return st;
-    hipLaunchKernelGGL(topkp_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, draft, part, T, V,
-                       n_chunks, top_k, inv_tau, (double)top_p, seed, request_id, pos0, out_tok, n_emit);
+    hipLaunchKernelGGL(topkp_set_kernel, dim3(B * T), dim3(kVerifyThreads), 0, stream, part, n_chunks, top_k,
+                       inv_tau, (double)top_p, sets);
+    st = launch_status();
+    if (st != DFLASH_OK) return st;
+    hipLaunchKernelGGL(topkp_decide_kernel, dim3(B), dim3(64), 0, stream, draft, sets, T, seed, request_id, pos0,
+                       out_tok, n_emit);
     return launch_status();
 }
 

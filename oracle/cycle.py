@@ -5,7 +5,10 @@ le papier"; latenode.com "DFlash 2: un drafter de 3.43×…", opening section):
 the drafter's convs (one call per drafter layer), the draft LM head with the
 top-16 lists, the pair selector's path, then verification of that path against
 the target's block logits.  "mixed" verification sends the first half of the
-requests to the greedy rule and the second half to rejection sampling.
+requests to the greedy rule and the second half to rejection sampling;
+with top_k > 0 the sampled requests are verified against the top-k, then
+top-p filtered target (latenode.com, FAQ: the published figures sample with
+top-p 0.95 and top-k 20).
 """
 
 import numpy as np
@@ -13,10 +16,10 @@ import numpy as np
 from .conv import conv2tap
 from .head import head_topk
 from .selector import select_path
-from .verify import verify_greedy, verify_sample
+from .verify import verify_greedy, verify_sample, verify_sample_topkp
 
 
-def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192):
+def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=1.0):
     L = inp["x"].shape[0]
     ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
     vals, idx, _ = head_topk(inp["h"], inp["W"], K=K, chunk=head_chunk)
@@ -30,7 +33,10 @@ def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192):
     g = {"greedy": B, "sample": 0, "mixed": B // 2}[verify]
     if g > 0:
         out[:g], n[:g] = verify_greedy(logits[:g], tok[:g])
-    if g < B:
+    if g < B and top_k > 0:
+        out[g:], n[g:] = verify_sample_topkp(logits[g:], tok[g:], inp["temperature"], top_k, top_p, inp["seed"],
+                                             inp["request_id"][g:], inp["pos0"][g:])
+    elif g < B:
         out[g:], n[g:] = verify_sample(logits[g:], tok[g:], inp["temperature"], inp["seed"],
                                        inp["request_id"][g:], inp["pos0"][g:])
     return {"y": ys, "top_val": vals, "top_idx": idx, "path_rank": rank,

@@ -19,7 +19,8 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-HEAD_SRC = os.path.join(ROOT, "block_draft_verification_amd", "csrc", "head_topk.hip")
+# the head kernels' sources: the kernel file and the key-sort header it includes
+HEAD_SRC = [os.path.join(ROOT, "block_draft_verification_amd", "csrc", f) for f in ("head_topk.hip", "keysort.hpp")]
 TRAFFIC = os.path.join(ROOT, "profiles", "head_topk_traffic.json")
 
 
@@ -71,7 +72,11 @@ def traffic(config, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, co
         wb = w.get(k, 0.0) * 1024.0 * w_scale
         kern[k] = {"fetch_bytes": int(fb), "write_bytes": int(wb)}
         total += fb + wb
-    sha = hashlib.sha256(open(HEAD_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in HEAD_SRC:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()[:16]
     try:
         rec = json.load(open(TRAFFIC))
     except (OSError, ValueError):
@@ -85,7 +90,7 @@ def traffic(config, fetch_csv, write_csv, cfetch_csv, cwrite_csv, copy_bytes, co
           f"Commands:\n\n```\n{commands}\n```\n",
           f"Counters are rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each taken in a run of its own "
           f"and scaled by what the same counter reads for a plain {int(copy_bytes)}-byte device copy "
-          f"(`{ck}`): fetch x{f_scale:.4f}, write x{w_scale:.4f}.  Head kernel source sha256[:16] = `{sha}`.\n",
+          f"(`{ck}`): fetch x{f_scale:.4f}, write x{w_scale:.4f}.  Head kernel sources (head_topk.hip and keysort.hpp) sha256[:16] = `{sha}`.\n",
           "| kernel | fetched bytes | written bytes |", "|---|---:|---:|"]
     for k, v in kern.items():
         md.append(f"| `{k}` | {v['fetch_bytes']:,} | {v['write_bytes']:,} |")

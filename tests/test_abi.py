@@ -152,7 +152,7 @@ def test_verify_topkp_validation():
     n = ctypes.c_size_t(0)
     q = lambda B, T, V, tau, k, p: f(A[0], A[1], B, T, V, tau, k, p, 0, A[4], A[5], A[2], A[3], NULL,
                                      ctypes.byref(n), NULL)
-    assert q(8, 8, 151936, 1.0, 20, 0.95) == OK and n.value == 8 * 8 * 38 * 20 * 8
+    assert q(8, 8, 151936, 1.0, 20, 0.95) == OK and n.value == 8 * 8 * 38 * 20 * 8 + 8 * 8 * 784
     for bad in [(8, 8, 100, 1.0, 0, 0.95), (8, 8, 100, 1.0, 65, 0.95), (8, 8, 100, 1.0, 20, 0.0),
                 (8, 8, 100, 1.0, 20, 1.5), (8, 8, 100, 1.0, 20, float("nan")), (8, 8, 100, 0.0, 20, 0.9),
                 (8, 17, 100, 1.0, 20, 0.9), (8, 1, 100, 1.0, 20, 0.9), (0, 8, 100, 1.0, 20, 0.9)]:

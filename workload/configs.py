@@ -26,6 +26,8 @@ class Config:
     plant_alpha: float = 0.0  # margin planted toward a random token per draft row
     agree_frac: float = 0.8   # context copy: fraction of slots where target argmax = draft top-1
     temperature: float = 1.0
+    top_k: int = 0            # sampled rows: 0 = full softmax, else top-k then top-p filtering
+    top_p: float = 1.0
     K: int = 16
     L: int = 5        # conv layer calls per cycle
     seed: int = 0
