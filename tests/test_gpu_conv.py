@@ -49,3 +49,15 @@ def test_conv_rejects_aliasing(dfl, dev):
     taps = rand_bf16((1, 8, 128), 4).to(dev)
     with pytest.raises(dfl.DFlashError):
         dfl.conv2tap(x, taps, out=x)
+
+
+@pytest.mark.parametrize("S,T,D", [(160, 16, 5120), (301, 7, 4096), (130, 13, 5120), (2100, 1, 4096),
+                                   (132, 16, 5000)])
+def test_conv_large_calls_four_rows_per_thread(dfl, dev, S, T, D):
+    """Calls of at least 2^20 threads take four token rows per thread; groups
+    of four straddle sequence starts when T is not a multiple of four, and the
+    last group is ragged."""
+    x = rand_bf16((S, T, D), S + T)
+    taps = rand_bf16((S, T, 2 * D), S + T + 1, sd=1.4)
+    y = dfl.conv2tap(x.to(dev), taps.to(dev)).cpu()
+    assert torch.equal(y.view(torch.int16), oracle_conv(x, taps).view(torch.int16))
