@@ -273,10 +273,12 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(
     for (int i = 1; i < kPerThread; ++i) m = fmaxf(m, v[i]);
     m = block_max(m, smax);
     const double md = (double)m;
+    // branch-free: an entry past the row end weighs exp(-inf) = 0, so all 16
+    // exponentials are scheduled together and share their constants
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i)
-        if (idx[i] != 0x7FFFFFFF) s += exp(((double)v[i] - md) * inv_tau);
+        s += exp(idx[i] != 0x7FFFFFFF ? ((double)v[i] - md) * inv_tau : -INFINITY);
     s = block_sum(s, ssum);
     if (threadIdx.x == 0) {
         ChunkStat cs;
