@@ -523,14 +523,20 @@ __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t
 // from LDS and the accumulators stay in registers.  A strip as wide as the
 // M-block makes re-reading h from L2 cost no more than streaming W.  The
 // top-16 epilogue's candidate buffers reuse the chunk tile's LDS.
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
 struct WideCfg {
     static constexpr int THREADS = 128 * WN;          // 2 x WN wavefronts
     static constexpr int KC = 32 * KS;
     static constexpr int MB = 32 * MW;                // rows of h per workgroup
     static constexpr int NB = 16 * WN * NT;           // W rows per strip
-    static constexpr int ROWB = KC * 2 + kPitchPad;
+    // SWZ: unpadded rows whose 16-byte pieces are permuted (piece ^ (row & 6)),
+    // which keeps fragment reads free of bank conflicts (see piece_off) in
+    // 20 % less LDS than the padded pitch
+    static constexpr int ROWB = KC * 2 + (SWZ ? 0 : kPitchPad);
     static constexpr int PIECES = KC / 8;             // 16-byte pieces per row and chunk
+    static_assert(!SWZ || PIECES == 8, "the swizzle is laid out for 8 pieces per row");
+    // byte offset of piece pc of tile row `row` inside the row
+    static __device__ __forceinline__ int piece_off(int row, int pc) { return (SWZ ? (pc ^ (row & 6)) : pc) * 16; }
     static constexpr int RPL = THREADS / PIECES;      // rows per workgroup-wide load
     static constexpr int HLOADS = (MB + RPL - 1) / RPL;
     static constexpr int WLOADS = NB / RPL;
@@ -553,12 +559,12 @@ __device__ __forceinline__ void with_slot(int k, F&& f) {
     }
 }
 
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t M, int D,
                       int64_t V, int64_t n_tiles, int S, int n_mb, float* __restrict__ part_val,
                       int* __restrict__ part_idx) {
-    using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
+    using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
     constexpr int KC = C::KC;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* lp = smem + C::LDS_BUF;
@@ -640,27 +646,30 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
             for (int q = 0; q < C::HLOADS; ++q) {
                 const int row = q * C::RPL + ri;
                 if (C::MB % C::RPL == 0 || row < C::MB)
-                    *reinterpret_cast<u32x4*>(tb + row * C::ROWB + pj * 16) = hq[j][q];
+                    *reinterpret_cast<u32x4*>(tb + row * C::ROWB + C::piece_off(row, pj)) = hq[j][q];
             }
             unsigned char* wb = tb + C::MB * C::ROWB;
 #pragma unroll
             for (int q = 0; q < C::WLOADS; ++q)
-                *reinterpret_cast<u32x4*>(wb + (q * C::RPL + ri) * C::ROWB + pj * 16) = wq[j][q];
+                *reinterpret_cast<u32x4*>(wb + (q * C::RPL + ri) * C::ROWB + C::piece_off(q * C::RPL + ri, pj)) =
+                    wq[j][q];
         };
         auto mfma_chunk = [&](int c, auto FULL) __attribute__((always_inline)) {
             constexpr bool full = decltype(FULL)::value;
             const unsigned char* tb = smem + (DBUF ? (size_t)(c & 1) * C::TILE : 0);
-            const unsigned char* ha = tb + (wm * 16 * MW + ln) * C::ROWB + lg * 16;
-            const unsigned char* wbp = tb + (C::MB + wn * 16 + ln) * C::ROWB + lg * 16;
+            // fragment rows start at multiples of 16, so (row & 6) == (ln & 6)
+            const unsigned char* ha = tb + (wm * 16 * MW + ln) * C::ROWB;
+            const unsigned char* wbp = tb + (C::MB + wn * 16 + ln) * C::ROWB;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
+                const int po = C::piece_off(ln, 4 * s + lg);
                 // all of the k-step's fragments first, then its MFMAs
                 u32x4 b[NT], a[MW];
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
-                    if (full || nt < nt_act) b[nt] = *reinterpret_cast<const u32x4*>(wbp + nt * 16 * WN * C::ROWB + 64 * s);
+                    if (full || nt < nt_act) b[nt] = *reinterpret_cast<const u32x4*>(wbp + nt * 16 * WN * C::ROWB + po);
 #pragma unroll
-                for (int mt = 0; mt < MW; ++mt) a[mt] = *reinterpret_cast<const u32x4*>(ha + mt * 16 * C::ROWB + 64 * s);
+                for (int mt = 0; mt < MW; ++mt) a[mt] = *reinterpret_cast<const u32x4*>(ha + mt * 16 * C::ROWB + po);
 #pragma unroll
                 for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
@@ -995,7 +1004,7 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
 // ------------------------------------------------------------------ host
 namespace {
 
-enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2 };
+enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3 };
 
 struct HeadPlan {
     HeadVariant variant;
@@ -1006,17 +1015,19 @@ struct HeadPlan {
 };
 
 // One instantiation of head_wide_kernel with its launch.
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
 struct WideVariant {
-    using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
-    static const void* fn() { return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN>); }
+    using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
+    static const void* fn() {
+        return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ>);
+    }
     static void set_attr() {
         (void)hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
     }
     static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
                        int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
         const int grid = (S + 7) / 8 * 8 * n_mb;
-        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN>), dim3(grid), dim3(Cfg::THREADS), Cfg::LDS, stream, h,
+        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ>), dim3(grid), dim3(Cfg::THREADS), Cfg::LDS, stream, h,
                            W, M, D, V, n_tiles, S, n_mb, pv, pi);
     }
 };
@@ -1030,6 +1041,9 @@ using SkinnyL = SkinnyLds<kSkinnyNT, kSkinnyKS, kSkinnyWaves>;
 // M = 480: 1400 us for four 128-row blocks, 1680 us for three 224-row ones).
 using Wide128 = WideVariant<4, 2, 2, 4, true, 4>;  // M-blocks of 128 rows
 using Wide224 = WideVariant<7, 2, 2, 2, true, 4>;  // M-blocks of 224 rows
+// several 128-row M-blocks (MFMA-bound sizes): 256-row strips in unpadded,
+// swizzled tiles, half the fragment reads per MFMA (M = 480: 1383 -> 1225 us)
+using Wide128W = WideVariant<4, 4, 2, 2, true, 4, true>;
 constexpr int kCUs = 256;
 
 HeadPlan head_plan(int64_t M, int64_t V) {
@@ -1049,6 +1063,9 @@ HeadPlan head_plan(int64_t M, int64_t V) {
     if (M > 128 && pad224 <= pad128) {
         p.variant = kWide224;
         p.mb_rows = Wide224::Cfg::MB;
+    } else if (M > 128) {
+        p.variant = kWide128W;
+        p.mb_rows = Wide128W::Cfg::MB;
     } else {
         p.variant = kWide128;
         p.mb_rows = Wide128::Cfg::MB;
@@ -1078,6 +1095,7 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkinnyL::BYTES);
         Wide128::set_attr();
         Wide224::set_attr();
+        Wide128W::set_attr();
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLists * kTopK * 8);
     });
@@ -1092,6 +1110,9 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
             break;
         case kWide128:
             Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            break;
+        case kWide128W:
+            Wide128W::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
         default:
             Wide224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);

@@ -30,7 +30,8 @@ def check(dfl, dev, h, W, rows=None):
 
 @pytest.mark.parametrize("M,D,V", [(1, 256, 4096), (7, 256, 4096), (7, 264, 4133), (16, 512, 1000),
                                    (17, 256, 5003), (56, 256, 4096), (65, 320, 3000), (128, 256, 2000),
-                                   (224, 256, 8192), (257, 256, 2048), (480, 128, 4096), (3, 8, 40)])
+                                   (224, 256, 8192), (257, 256, 2048), (480, 128, 4096), (300, 264, 3001),
+                                   (3, 8, 40)])
 def test_gaussian_shapes(dfl, dev, M, D, V):
     g = torch.Generator().manual_seed(M * 7 + D + V)
     h = torch.randn(M, D, generator=g).to(torch.bfloat16)
@@ -100,7 +101,7 @@ def test_planted_maxima(dfl, dev):
 
 
 @pytest.mark.parametrize("name,rows", [("c2_b1", None), ("c4_b32", [0, 1, 100, 223]),
-                                       ("c5_stress", [0, 239, 240, 479])])
+                                       ("c5_stress", [0, 127, 128, 239, 240, 383, 384, 479])])
 def test_full_size_configs(dfl, dev, name, rows):
     cfg = get_config(name)
     g = torch.Generator(device=dev).manual_seed(11)
