@@ -25,6 +25,12 @@ Readings taken (the pages give no formula):
 * Arithmetic is float64.  Each pair score is summed over k = 0..r-1 in index
   order (float32 x float32 products are exact in float64, so a fused or a
   separate multiply-add gives the same result at every step).
+* Anchored variant (a NEXT item of the blueprint, reading): slot 0 of the
+  block holds the last verified token a, known before drafting; it joins the
+  lattice as a one-node column in front of position 0, so
+      delta_0[i] = val[0][i] + pair(a, idx[0][i])
+  and everything else is unchanged.  An anchor id outside [0, V) has a zero
+  feature row (pair 0), like any other id.
 """
 
 import numpy as np
@@ -43,21 +49,26 @@ def pair_scores(idx_left, idx_right, F_l, F_r):
     return acc
 
 
-def select_path(top_val, top_idx, F_l, F_r):
+def select_path(top_val, top_idx, F_l, F_r, anchor=None):
     """Max-sum path per request.
 
     top_val: [B][P][K] float32 draft logits of the candidates, top_idx: [B][P][K]
-    vocab ids.  Returns (rank i32 [B][P], tok i32 [B][P], score f32 [B],
-    score f64 [B]).
+    vocab ids, anchor: optional [B] ids of the block's slot-0 tokens.  Returns
+    (rank i32 [B][P], tok i32 [B][P], score f32 [B], score f64 [B]).
     """
     val = f64(top_val)
     idx = i64(top_idx)
     B, P, K = val.shape
+    V = F_l.shape[0]
     rank = np.zeros((B, P), dtype=np.int32)
     tok = np.zeros((B, P), dtype=np.int32)
     score64 = np.zeros(B, dtype=np.float64)
     for b in range(B):
         delta = val[b, 0].copy()
+        if anchor is not None:
+            a = int(anchor[b])
+            if 0 <= a < V:
+                delta = delta + pair_scores([a], idx[b, 0], F_l, F_r)[0]
         psi = []
         for p in range(P - 1):
             pair = pair_scores(idx[b, p], idx[b, p + 1], F_l, F_r)

@@ -120,3 +120,48 @@ def test_reported_score_is_path_score_and_shift_invariant():
     shifted[:, 3] += np.float32(4.0)
     rank2, _, _, _ = select_path(shifted, idx, F_l, F_r)
     assert np.array_equal(rank, rank2)
+
+
+# ------------------------------------------------------------ anchored variant
+def brute_force_anchored(val, idx, F_l, F_r, a):
+    """Every path with the anchor's pair term on position 0 (library matmul)."""
+    extra = (F_l[[a]].astype(np.float64) @ F_r[idx[0]].astype(np.float64).T)[0]
+    v = val.astype(np.float64).copy()
+    v[0] = v[0] + extra
+    return brute_force(v, idx, F_l, F_r)
+
+
+@pytest.mark.parametrize("P", [1, 2, 3, 4])
+def test_anchored_against_brute_force(P):
+    val, idx, F_l, F_r = make_case(40 + P, 6, P)
+    anchor = np.random.default_rng(P).integers(0, F_l.shape[0], 6)
+    rank, tok, score, score64 = select_path(val, idx, F_l, F_r, anchor=anchor)
+    for b in range(6):
+        path, best, gap = brute_force_anchored(val[b], idx[b], F_l, F_r, int(anchor[b]))
+        if gap > 1e-9:
+            assert list(rank[b]) == list(path)
+        assert abs(score64[b] - best) <= 1e-9 * max(1.0, abs(best))
+
+
+def test_anchor_with_zero_features_or_outside_vocab_is_unanchored():
+    val, idx, F_l, F_r = make_case(7, 5, 4)
+    F_l0 = F_l.copy()
+    F_l0[3] = 0.0
+    plain = select_path(val, idx, F_l0, F_r)
+    zero = select_path(val, idx, F_l0, F_r, anchor=np.full(5, 3))
+    outside = select_path(val, idx, F_l0, F_r, anchor=np.array([-1, 300, 10**6, -7, 301]))
+    for r in (zero, outside):
+        assert np.array_equal(r[0], plain[0]) and np.array_equal(r[3], plain[3])
+
+
+def test_dominant_anchor_edge_fixes_the_first_choice():
+    """An anchor pair term far larger than everything else picks position 0's
+    candidate with the largest pair score with the anchor, then the
+    unanchored DP of the remaining positions given that start."""
+    val, idx, F_l, F_r = make_case(9, 4, 3, r=4)
+    F_l = F_l.copy()
+    F_l[5] = 0.0
+    F_l[5, 0] = 1000.0
+    rank, _, _, _ = select_path(val, idx, F_l, F_r, anchor=np.full(4, 5))
+    for b in range(4):
+        assert rank[b, 0] == int(np.argmax(F_r[idx[b, 0], 0]))
