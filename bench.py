@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--sample-top-k", type=int, default=0,
                     help="sampled requests: filter the target to its top-k, then top-p (0 = full softmax)")
     ap.add_argument("--sample-top-p", type=float, default=1.0)
+    ap.add_argument("--anchored", action="store_true",
+                    help="selector anchored on each block's slot-0 token")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -98,7 +100,8 @@ class CycleRunner:
         self.g = g
         u8 = torch.uint8
         self.ws_head = torch.empty(dfl.workspace_bytes("head_topk", cfg.M, cfg.D, cfg.V), dtype=u8, device=dev)
-        self.ws_sel = torch.empty(dfl.workspace_bytes("select_path", B, P), dtype=u8, device=dev)
+        self.ws_sel = torch.empty(dfl.workspace_bytes("select_path_anchored" if cfg.anchored else "select_path", B, P),
+                                  dtype=u8, device=dev)
         self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
         if cfg.top_k > 0:
             self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_topkp", max(B - g, 1), T, cfg.V, cfg.top_k),
@@ -116,7 +119,8 @@ class CycleRunner:
         tv3, ti3 = self.tv.view(B, cfg.P, 16), self.ti.view(B, cfg.P, 16)
         conv = [dfl.bind_conv2tap(s["x"], s["taps"], self.y_all)]
         head = dfl.bind_head_topk(s["h"], self.W, self.tv, self.ti, self.ws_head)
-        sel = dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel)
+        sel = dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel,
+                                   anchor=s["anchor"] if cfg.anchored else None)
         ver = []
         if g > 0:
             ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
@@ -174,7 +178,7 @@ class CycleRunner:
 def make_sets(torch, cfg, inp, max_sets):
     B, g = cfg.B, {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
     base = {
-        "x": inp["x"], "taps": inp["taps"], "h": inp["h"],
+        "x": inp["x"], "taps": inp["taps"], "h": inp["h"], "anchor": inp["anchor"],
         "target_g": inp["target"][:g].contiguous() if g > 0 else None,
         "target_s": inp["target"][g:].contiguous() if g < B else None,
         "rid_s": inp["request_id"][g:].contiguous(), "pos_s": inp["pos0"][g:].contiguous(),
@@ -242,12 +246,12 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
 
     host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     t0 = time.perf_counter()
-    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p)
+    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
     while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
-        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p)
+        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored)
         total += time.perf_counter() - t0
         n += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -284,7 +288,7 @@ def main():
 
     dfl.lib()
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p)
+    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored)
     log(f"[bench] config {cfg.name}: generating inputs on {dev}")
     inp = make_cycle_inputs(cfg, device=dev)
     sets, per_set = make_sets(torch, cfg, inp, args.max_sets)
@@ -361,7 +365,8 @@ def main():
         "config": {"workload": f"{cfg.name}: {WORKLOAD_TEXT[cfg.name]}", "batch": cfg.B, "block": cfg.T,
                    "hidden": cfg.D, "vocab": cfg.V, "top_k": 16, "selector_rank": cfg.r,
                    "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets),
-                   **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {})},
+                   **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {}),
+                   **({"selector": "anchored on slot 0"} if cfg.anchored else {})},
         "roofline": head_roofline(cfg, head_us),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),

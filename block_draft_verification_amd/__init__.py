@@ -31,6 +31,8 @@ _SIGNATURES = {
     "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
     "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                           _p, _p, _p, _p, _psz, _p]),
+    "dflash_select_path_anchored": (ctypes.c_int, [_p, _p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                                   _p, _p, _p, _p, _psz, _p]),
     "dflash_verify_greedy": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _p, _p, _p, _psz, _p]),
     "dflash_verify_sample": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p, _p,
                                             _p, _p, _p, _psz, _p]),
@@ -136,9 +138,10 @@ def head_topk(h, W, K=16, workspace=None, out=None):
     return tv, ti
 
 
-def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None):
+def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None, anchor=None):
     """top_val f32 [B][P][16], top_idx i32 [B][P][16], F_l/F_r f32 [V][r]
-    -> (path_rank i32 [B][P], path_tok i32 [B][P], path_score f32 [B])."""
+    -> (path_rank i32 [B][P], path_tok i32 [B][P], path_score f32 [B]).
+    With anchor (i32 [B], the blocks' slot-0 tokens) the anchored selector runs."""
     _need(top_val, torch.float32, "top_val", 3)
     _need(top_idx, torch.int32, "top_idx", 3)
     _need(F_l, torch.float32, "F_l", 2)
@@ -147,6 +150,10 @@ def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None):
     V, r = F_l.shape
     if tuple(F_r.shape) != (V, r) or tuple(top_idx.shape) != (B, P, K):
         raise DFlashError("shape mismatch in select_path")
+    if anchor is not None:
+        _need(anchor, torch.int32, "anchor", 1)
+        if anchor.numel() != B:
+            raise DFlashError("anchor must hold one id per request")
     if out is None:
         rank = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
         tok = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
@@ -154,12 +161,16 @@ def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None):
     else:
         rank, tok, score = out
     L = lib()
-    before = (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
-              _ptr(score))
-    ws, nbytes = _workspace(L.dflash_select_path, before, (_stream(top_val.device),), top_val.device,
-                            workspace)
-    _check(L.dflash_select_path(*before, _ptr(ws), ctypes.byref(nbytes), _stream(top_val.device)),
-           "dflash_select_path")
+    if anchor is None:
+        fn, name = L.dflash_select_path, "dflash_select_path"
+        before = (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
+                  _ptr(score))
+    else:
+        fn, name = L.dflash_select_path_anchored, "dflash_select_path_anchored"
+        before = (_ptr(top_val), _ptr(top_idx), _ptr(anchor), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank),
+                  _ptr(tok), _ptr(score))
+    ws, nbytes = _workspace(fn, before, (_stream(top_val.device),), top_val.device, workspace)
+    _check(fn(*before, _ptr(ws), ctypes.byref(nbytes), _stream(top_val.device)), name)
     return rank, tok, score
 
 
@@ -270,14 +281,20 @@ def bind_head_topk(h, W, top_val, top_idx, workspace):
                    _ptr(workspace), ctypes.byref(nbytes), _stream(h.device)), "dflash_head_topk")
 
 
-def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score, workspace):
+def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score, workspace, anchor=None):
     B, P, K = top_val.shape
     V, r = F_l.shape
     nbytes = ctypes.c_size_t(workspace.numel())
-    return _bound(lib().dflash_select_path,
-                  (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
-                   _ptr(score), _ptr(workspace), ctypes.byref(nbytes), _stream(top_val.device)),
-                  "dflash_select_path")
+    if anchor is None:
+        return _bound(lib().dflash_select_path,
+                      (_ptr(top_val), _ptr(top_idx), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank), _ptr(tok),
+                       _ptr(score), _ptr(workspace), ctypes.byref(nbytes), _stream(top_val.device)),
+                      "dflash_select_path")
+    _need(anchor, torch.int32, "anchor", 1)
+    return _bound(lib().dflash_select_path_anchored,
+                  (_ptr(top_val), _ptr(top_idx), _ptr(anchor), _ptr(F_l), _ptr(F_r), B, P, K, V, r, _ptr(rank),
+                   _ptr(tok), _ptr(score), _ptr(workspace), ctypes.byref(nbytes), _stream(top_val.device)),
+                  "dflash_select_path_anchored")
 
 
 def bind_verify_greedy(logits, draft, out_tok, n_emit, workspace):
@@ -309,7 +326,8 @@ def bind_verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, req
 
 def workspace_bytes(op, *shape_args):
     """Workspace size of an entry point for the given sizes, without a GPU call:
-    op in {"head_topk": (M, D, V), "select_path": (B, P), "verify_greedy": (B, T, V),
+    op in {"head_topk": (M, D, V), "select_path": (B, P), "select_path_anchored": (B, P),
+    "verify_greedy": (B, T, V),
     "verify_sample": (B, T, V), "verify_sample_topkp": (B, T, V, top_k)}."""
     L = lib()
     n = ctypes.c_size_t(0)
@@ -321,6 +339,10 @@ def workspace_bytes(op, *shape_args):
         B, P = shape_args
         code = L.dflash_select_path(fake[0], fake[1], fake[2], fake[3], B, P, 16, 1024, 16, fake[4], fake[5],
                                     fake[6], None, ctypes.byref(n), None)
+    elif op == "select_path_anchored":
+        B, P = shape_args
+        code = L.dflash_select_path_anchored(fake[0], fake[1], fake[7], fake[2], fake[3], B, P, 16, 1024, 16,
+                                             fake[4], fake[5], fake[6], None, ctypes.byref(n), None)
     elif op == "verify_greedy":
         B, T, V = shape_args
         code = L.dflash_verify_greedy(fake[0], fake[1], B, T, V, fake[2], fake[3], None, ctypes.byref(n), None)

@@ -15,9 +15,9 @@ int launch_conv2tap(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, i
 int launch_head_topk(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*, void*,
                      hipStream_t);
 size_t head_workspace_bytes(int64_t M, int64_t V);
-int launch_select_path(const float*, const int32_t*, const float*, const float*, int, int, int64_t, int,
-                       int32_t*, int32_t*, float*, void*, hipStream_t);
-size_t select_workspace_bytes(int B, int P);
+int launch_select_path(const float*, const int32_t*, const int32_t*, const float*, const float*, int, int, int64_t,
+                       int, int32_t*, int32_t*, float*, void*, hipStream_t);
+size_t select_workspace_bytes(int B, int P, bool anchored);
 size_t greedy_workspace_bytes(int B, int T, int64_t V);
 size_t sample_workspace_bytes(int B, int T, int64_t V);
 size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k);
@@ -129,12 +129,13 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
     return launch_head_topk(h, W, M, D, V, top_val, top_idx, workspace, (hipStream_t)stream);
 }
 
-int dflash_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
-                       const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
-                       int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
-                       size_t* workspace_bytes, void* stream) {
+static int select_common(const float* top_val, const int32_t* top_idx, const int32_t* anchor, bool anchored,
+                         const float* feat_l, const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V,
+                         int32_t r, int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
+                         size_t* workspace_bytes, void* stream) {
     if (!top_val || !top_idx || !feat_l || !feat_r || !path_rank || !path_tok || !path_score)
         return DFLASH_ERR_INVALID;
+    if (anchored && (!anchor || !aligned4(anchor))) return DFLASH_ERR_INVALID;
     if (B < 1 || P < 1 || P > 15 || V < 1 || r < 4 || r > 256 || r % 4 != 0) return DFLASH_ERR_INVALID;
     if (K != 16) return DFLASH_ERR_UNSUPPORTED;
     if (!aligned4(top_val) || !aligned4(top_idx) || !aligned16(feat_l) || !aligned16(feat_r) ||
@@ -143,26 +144,42 @@ int dflash_select_path(const float* top_val, const int32_t* top_idx, const float
     const size_t nbp = (size_t)B * P * 4, nin = (size_t)B * P * K * 4;
     const void* outs[3] = {path_rank, path_tok, path_score};
     const size_t outn[3] = {nbp, nbp, (size_t)B * 4};
-    const void* ins[4] = {top_val, top_idx, feat_l, feat_r};
-    const size_t inn[4] = {nin, nin, (size_t)V * r * 4, (size_t)V * r * 4};
+    const void* ins[5] = {top_val, top_idx, feat_l, feat_r, anchor};
+    const size_t inn[5] = {nin, nin, (size_t)V * r * 4, (size_t)V * r * 4, anchored ? (size_t)B * 4 : 0};
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 5; ++j)
             if (overlap(outs[i], outn[i], ins[j], inn[j])) return DFLASH_ERR_INVALID;
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outn[i], outs[j], outn[j])) return DFLASH_ERR_INVALID;
     }
     bool query = false;
-    int st = workspace_check(workspace, workspace_bytes, select_workspace_bytes(B, P), &query);
+    int st = workspace_check(workspace, workspace_bytes, select_workspace_bytes(B, P, anchored), &query);
     if (st != DFLASH_OK || query) return st;
     const size_t nws = *workspace_bytes;
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 5; ++j)
         if (overlap(workspace, nws, ins[j], inn[j])) return DFLASH_ERR_INVALID;
     for (int i = 0; i < 3; ++i)
         if (overlap(workspace, nws, outs[i], outn[i])) return DFLASH_ERR_INVALID;
     st = check_device();
     if (st != DFLASH_OK) return st;
-    return launch_select_path(top_val, top_idx, feat_l, feat_r, B, P, V, r, path_rank, path_tok, path_score,
-                              workspace, (hipStream_t)stream);
+    return launch_select_path(top_val, top_idx, anchored ? anchor : nullptr, feat_l, feat_r, B, P, V, r, path_rank,
+                              path_tok, path_score, workspace, (hipStream_t)stream);
+}
+
+int dflash_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
+                       const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
+                       int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
+                       size_t* workspace_bytes, void* stream) {
+    return select_common(top_val, top_idx, nullptr, false, feat_l, feat_r, B, P, K, V, r, path_rank, path_tok,
+                         path_score, workspace, workspace_bytes, stream);
+}
+
+int dflash_select_path_anchored(const float* top_val, const int32_t* top_idx, const int32_t* anchor,
+                                const float* feat_l, const float* feat_r, int32_t B, int32_t P, int32_t K,
+                                int64_t V, int32_t r, int32_t* path_rank, int32_t* path_tok, float* path_score,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
+    return select_common(top_val, top_idx, anchor, true, feat_l, feat_r, B, P, K, V, r, path_rank, path_tok,
+                         path_score, workspace, workspace_bytes, stream);
 }
 
 static int verify_common_checks(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,

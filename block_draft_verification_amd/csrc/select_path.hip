@@ -30,19 +30,27 @@ constexpr int kMaxP = 15;
 constexpr int kMaxVec = 4;         // float4s per thread per table: 16 rows x r <= 256 floats / 256 threads
 constexpr int kPitch = kTopK + 1;  // floats per k in the staged tables
 
+// Tiles p < P-1: pairs (p, p+1).  With an anchor, tile P-1 scores the
+// request's anchor token (every row) against position 0's candidates.
 __global__ __launch_bounds__(256) void select_pairs_kernel(const int32_t* __restrict__ top_idx,
+                                                           const int32_t* __restrict__ anchor,
                                                            const float* __restrict__ feat_l,
                                                            const float* __restrict__ feat_r, int P, int64_t V,
-                                                           int r, double* __restrict__ pairs) {
+                                                           int r, int n_tiles, double* __restrict__ pairs) {
     __shared__ float sl[256 * kPitch];
     __shared__ float sr[256 * kPitch];
     __shared__ int il_s[kTopK], ir_s[kTopK];
-    const int p = blockIdx.x;   // pair (p, p+1)
+    const int p = blockIdx.x;   // tile
     const int b = blockIdx.y;   // request
     const int lt = threadIdx.x;
     if (lt < kTopK) {
-        il_s[lt] = top_idx[((int64_t)b * P + p) * kTopK + lt];
-        ir_s[lt] = top_idx[((int64_t)b * P + p + 1) * kTopK + lt];
+        if (p == P - 1) {  // the anchor tile (only launched with an anchor)
+            il_s[lt] = anchor[b];
+            ir_s[lt] = top_idx[(int64_t)b * P * kTopK + lt];
+        } else {
+            il_s[lt] = top_idx[((int64_t)b * P + p) * kTopK + lt];
+            ir_s[lt] = top_idx[((int64_t)b * P + p + 1) * kTopK + lt];
+        }
     }
     __syncthreads();
     const int r4 = r >> 2;
@@ -77,13 +85,13 @@ __global__ __launch_bounds__(256) void select_pairs_kernel(const int32_t* __rest
     double acc = 0.0;
 #pragma unroll 16
     for (int k = 0; k < r; ++k) acc = fma((double)sl[k * kPitch + i], (double)sr[k * kPitch + j], acc);
-    pairs[(((int64_t)b * (P - 1) + p) * kTopK + i) * kTopK + j] = acc;
+    pairs[(((int64_t)b * n_tiles + p) * kTopK + i) * kTopK + j] = acc;
 }
 
 __global__ __launch_bounds__(64) void select_dp_kernel(const float* __restrict__ top_val,
                                                        const int32_t* __restrict__ top_idx,
-                                                       const double* __restrict__ pairs, int P,
-                                                       int32_t* __restrict__ path_rank,
+                                                       const double* __restrict__ pairs, int P, int n_tiles,
+                                                       bool anchored, int32_t* __restrict__ path_rank,
                                                        int32_t* __restrict__ path_tok,
                                                        float* __restrict__ path_score) {
     __shared__ double val_s[kMaxP][kTopK];
@@ -92,9 +100,11 @@ __global__ __launch_bounds__(64) void select_dp_kernel(const float* __restrict__
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     for (int e = tid; e < P * kTopK; e += 64) val_s[e / kTopK][e % kTopK] = (double)top_val[(int64_t)b * P * kTopK + e];
-    if (tid < kTopK) delta[tid] = (double)top_val[(int64_t)b * P * kTopK + tid];
+    const double* pb = pairs + (int64_t)b * n_tiles * kTopK * kTopK;
+    if (tid < kTopK)
+        delta[tid] = (double)top_val[(int64_t)b * P * kTopK + tid] +
+                     (anchored ? pb[(int64_t)(P - 1) * kTopK * kTopK + tid] : 0.0);
     __syncthreads();
-    const double* pb = pairs + (int64_t)b * (P - 1) * kTopK * kTopK;
     for (int p = 0; p + 1 < P; ++p) {
         double nd = 0.0;
         if (tid < kTopK) {
@@ -134,20 +144,24 @@ __global__ __launch_bounds__(64) void select_dp_kernel(const float* __restrict__
     }
 }
 
-size_t select_workspace_bytes(int B, int P) { return (size_t)B * (P > 1 ? P - 1 : 1) * kTopK * kTopK * 8; }
+size_t select_workspace_bytes(int B, int P, bool anchored) {
+    const int n_tiles = P - 1 + (anchored ? 1 : 0);
+    return (size_t)B * (n_tiles > 0 ? n_tiles : 1) * kTopK * kTopK * 8;
+}
 
-int launch_select_path(const float* top_val, const int32_t* top_idx, const float* feat_l,
+int launch_select_path(const float* top_val, const int32_t* top_idx, const int32_t* anchor, const float* feat_l,
                        const float* feat_r, int B, int P, int64_t V, int r, int32_t* path_rank,
                        int32_t* path_tok, float* path_score, void* ws, hipStream_t stream) {
     double* pairs = reinterpret_cast<double*>(ws);
-    if (P > 1) {
-        hipLaunchKernelGGL(select_pairs_kernel, dim3(P - 1, B), dim3(256), 0, stream, top_idx, feat_l, feat_r, P, V,
-                           r, pairs);
+    const int n_tiles = P - 1 + (anchor ? 1 : 0);
+    if (n_tiles > 0) {
+        hipLaunchKernelGGL(select_pairs_kernel, dim3(n_tiles, B), dim3(256), 0, stream, top_idx, anchor, feat_l,
+                           feat_r, P, V, r, n_tiles, pairs);
         const int st = launch_status();
         if (st != DFLASH_OK) return st;
     }
-    hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(64), 0, stream, top_val, top_idx, pairs, P, path_rank,
-                       path_tok, path_score);
+    hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(64), 0, stream, top_val, top_idx, pairs, P, n_tiles,
+                       anchor != nullptr, path_rank, path_tok, path_score);
     return launch_status();
 }
 

@@ -10,10 +10,12 @@
  *   dflash_verify_greedy  greedy longest-prefix acceptance
  *   dflash_verify_sample  rejection-sampling acceptance (Philox4x64-10 draws)
  *
- * and one variant of the last step:
+ * and two variants:
  *
- *   dflash_verify_sample_topkp  rejection sampling against a top-k / top-p
- *                               filtered target
+ *   dflash_select_path_anchored  the selector with the block's slot-0 token as
+ *                                a fixed first column
+ *   dflash_verify_sample_topkp   rejection sampling against a top-k / top-p
+ *                                filtered target
  *
  * Sources (the pages describe the method in words only):
  *   tamsi.dev, "DFlash 2 - 3x plus de tokens sur Qwen3.8-27B, meme sortie",
@@ -142,6 +144,26 @@ int dflash_select_path(const float* top_val, const int32_t* top_idx,
                        int32_t B, int32_t P, int32_t K, int64_t V, int32_t r,
                        int32_t* path_rank, int32_t* path_tok, float* path_score,
                        void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Pair selector anchored on the block's slot-0 token.
+ * Source: as dflash_select_path (the pages describe scoring adjacent
+ * positions so that the block is coherent; slot 0, the last verified token,
+ * is the block's first position).  Reading: the anchor a = anchor[b] joins the
+ * lattice as a one-node column before position 0,
+ *     delta_0[i] = val[0][i] + pair(a, idx[0][i]),
+ * everything else as dflash_select_path; an anchor outside [0, V) scores 0.
+ *   anchor  i32 [B]   slot-0 token per request
+ *   other arguments as for dflash_select_path.
+ * Requires as dflash_select_path.  Workspace: B*P*16*16 doubles (the pair
+ * tiles plus one anchor tile per request).
+ */
+int dflash_select_path_anchored(const float* top_val, const int32_t* top_idx,
+                                const int32_t* anchor, const float* feat_l,
+                                const float* feat_r, int32_t B, int32_t P, int32_t K,
+                                int64_t V, int32_t r, int32_t* path_rank,
+                                int32_t* path_tok, float* path_score, void* workspace,
+                                size_t* workspace_bytes, void* stream);
 
 /*
  * Greedy verification.

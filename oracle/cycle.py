@@ -8,7 +8,8 @@ the target's block logits.  "mixed" verification sends the first half of the
 requests to the greedy rule and the second half to rejection sampling;
 with top_k > 0 the sampled requests are verified against the top-k, then
 top-p filtered target (latenode.com, FAQ: the published figures sample with
-top-p 0.95 and top-k 20).
+top-p 0.95 and top-k 20); with anchored=True the selector starts from each
+block's slot-0 token.
 """
 
 import numpy as np
@@ -19,14 +20,15 @@ from .selector import select_path
 from .verify import verify_greedy, verify_sample, verify_sample_topkp
 
 
-def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=1.0):
+def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=1.0, anchored=False):
     L = inp["x"].shape[0]
     ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
     vals, idx, _ = head_topk(inp["h"], inp["W"], K=K, chunk=head_chunk)
     P = T - 1
     vals = vals.reshape(B, P, K)
     idx = idx.reshape(B, P, K)
-    rank, tok, score, _ = select_path(vals, idx, inp["F_l"], inp["F_r"])
+    anchor = inp["anchor"] if anchored else None
+    rank, tok, score, _ = select_path(vals, idx, inp["F_l"], inp["F_r"], anchor=anchor)
     logits = inp["target"]
     out = np.full((B, T), -1, np.int32)
     n = np.zeros(B, np.int32)

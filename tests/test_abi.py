@@ -164,3 +164,20 @@ def test_verify_topkp_validation():
         ok = ctypes.c_size_t(n.value)
         assert f(A[0], A[1], 8, 8, 151936, 1.0, 20, 0.95, 0, A[4], A[5], A[2], A[3], A[6], ctypes.byref(ok),
                  NULL) == DEVICE
+
+
+@needs_lib
+def test_select_anchored_validation():
+    f = dfl.lib().dflash_select_path_anchored
+    n = ctypes.c_size_t(0)
+    args = lambda B, P, K, V, r, anchor=A[8], out0=A[4], ws=NULL: (A[0], A[1], anchor, A[2], A[3], B, P, K, V, r,
+                                                                   out0, A[5], A[6], ws, ctypes.byref(n), NULL)
+    assert f(*args(4, 7, 16, 4096, 32)) == OK and n.value == 4 * 7 * 16 * 16 * 8
+    assert f(*args(4, 1, 16, 4096, 32)) == OK and n.value == 4 * 1 * 16 * 16 * 8
+    assert f(*args(4, 7, 16, 4096, 32, anchor=NULL)) == INVALID
+    assert f(*args(4, 7, 16, 4096, 32, anchor=ctypes.c_void_p((9 << 40) + 2))) == INVALID   # misaligned
+    assert f(*args(4, 7, 8, 4096, 32)) == UNSUPPORTED
+    assert f(*args(4, 7, 16, 4096, 32, out0=A[8])) == INVALID                             # output on the anchor
+    if not torch.cuda.is_available():
+        n.value = 1 << 20
+        assert f(*args(2, 7, 16, 4096, 192, ws=A[7])) == DEVICE

@@ -72,3 +72,38 @@ def test_batch32_block8_shapes(dfl, dev):
     rank, tok, score = run(dfl, dev, val, idx, F_l, F_r)
     r0, t0, s0, _ = oracle_select(val, idx, F_l, F_r)
     assert np.array_equal(rank, r0) and np.array_equal(tok, t0) and np.array_equal(score, s0)
+
+
+# ------------------------------------------------------------ anchored selector
+def run_anchored(dfl, dev, val, idx, F_l, F_r, anchor):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rank, tok, score = dfl.select_path(t(val), t(idx), t(F_l), t(F_r), anchor=t(anchor.astype(np.int32)))
+    torch.cuda.synchronize()
+    return rank.cpu().numpy(), tok.cpu().numpy(), score.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,P,V,r", [(4, 1, 100, 4), (4, 2, 100, 8), (5, 7, 4096, 32), (2, 7, 4096, 192),
+                                     (2, 15, 4096, 192), (32, 7, 151936, 192)])
+def test_anchored_matches_oracle(dfl, dev, B, P, V, r):
+    val, idx, F_l, F_r = lattice(B * 13 + P + r, B, P, V, r)
+    anchor = np.random.default_rng(P + r).integers(0, V, B)
+    if B >= 3:
+        anchor[:3] = [-1, V, 5 * V]              # outside the vocabulary: pair 0
+    rank, tok, score = run_anchored(dfl, dev, val, idx, F_l, F_r, anchor)
+    r0, t0, s0, _ = oracle_select(val, idx, F_l, F_r, anchor=anchor)
+    assert np.array_equal(rank, r0) and np.array_equal(tok, t0) and np.array_equal(score, s0)
+
+
+def test_anchor_changes_the_path_only_through_position_0(dfl, dev):
+    """A dominant anchor edge fixes position 0 to the candidate pairing best
+    with the anchor; an anchor whose feature row is zero reproduces the
+    unanchored selector."""
+    val, idx, F_l, F_r = lattice(77, 6, 7, 2000, 16)
+    F_l = F_l.copy()
+    F_l[11] = 0.0
+    plain = run(dfl, dev, val, idx, F_l, F_r)
+    zero = run_anchored(dfl, dev, val, idx, F_l, F_r, np.full(6, 11))
+    assert all(np.array_equal(a, b) for a, b in zip(plain, zero))
+    F_l[11, 0] = 1e4
+    rank, _, _ = run_anchored(dfl, dev, val, idx, F_l, F_r, np.full(6, 11))
+    assert np.array_equal(rank[:, 0], np.argmax(F_r[idx[:, 0], 0], axis=1))

@@ -133,11 +133,14 @@ def make_cycle_inputs(cfg, device="cpu"):
     else:
         raise ValueError(cfg.logits)
 
+    # the blocks' slot-0 tokens (the last verified token of each request), for
+    # the anchored selector
+    anchor = torch.randint(0, V, (B,), generator=gen("anchor"), device=dev, dtype=torch.int64).to(torch.int32)
     request_id = torch.arange(B, dtype=torch.int64, device=dev)
     pos0 = 4096 + 64 * torch.arange(B, dtype=torch.int64, device=dev)
     return {
         "x": x, "taps": taps, "h": h, "W": W, "F_l": F_l, "F_r": F_r,
-        "target": target, "request_id": request_id, "pos0": pos0,
+        "target": target, "request_id": request_id, "pos0": pos0, "anchor": anchor,
         "planted": planted, "temperature": float(cfg.temperature),
         "seed": int(cfg.seed),
     }
