@@ -37,6 +37,13 @@ __device__ __forceinline__ bool ranks_before_d(double va, int ia, double vb, int
     return va > vb || (va == vb && ia < ib);
 }
 
+// Orders the LDS accesses of one wavefront around this point.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Kernel launch helpers (host side).
 inline int launch_status() {
     hipError_t e = hipGetLastError();

@@ -68,12 +68,6 @@ __device__ __forceinline__ u32x4 ldg_stream(const uint16_t* p) {
 }
 __device__ __forceinline__ u32x4 ldg(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Bitonic sort over groups of WIDTH lanes (WIDTH = 32 or 64), descending in the
 // ranks_before order.
 template <int WIDTH>
@@ -331,14 +325,13 @@ constexpr int kOffNone = 0x7FFFFFF0;      // a lane offset outside every resourc
 // fragments.  h rows past M and W rows past V come back as zeros.
 template <int NTX, int KS>
 __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const uint16_t* __restrict__ W,
-                                              int64_t M, int D, int64_t V, int64_t t0, TopkRows tk,
+                                              int64_t M, int D, int64_t V, int64_t row0, TopkRows tk,
                                               unsigned char* __restrict__ wl) {
     using C = Skinny2Cfg<NTX, KS>;
     constexpr int KC = C::KC;
     const int lane = threadIdx.x & 63;
     const int ln = lane & 15, lg = lane >> 4;
     const int ri = lane / C::PIECES, pj = lane % C::PIECES;
-    const int64_t row0 = t0 * 16;
     const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(W + row0 * D, (V - row0) * D * 2);
     // The row goes into the lane offset (range-checked against the resource),
     // the chunk's column offset into the scalar offset.
@@ -423,7 +416,7 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
         stage(w0, h0);
         compute();
     }
-    topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, t0 * 16, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
+    topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, row0, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
 }
 
 // WAVES wavefronts per workgroup (4 or 8).
@@ -439,7 +432,7 @@ struct SkinnyLds {
 template <int NT, int KS, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t* __restrict__ h,
                                                                  const uint16_t* __restrict__ W, int64_t M,
-                                                                 int D, int64_t V, int64_t n_tiles,
+                                                                 int D, int64_t V,
                                                                  float* __restrict__ part_val,
                                                                  int* __restrict__ part_idx) {
     using C = Skinny2Cfg<NT, KS>;
@@ -467,14 +460,19 @@ __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t
     topk_init(tk, 16, lane, 64);
     wave_sync();
 
+    // Each wavefront owns a contiguous range of vocabulary rows, balanced to
+    // within one row (not whole 16-row tiles, whose count per wavefront would
+    // differ by one tile): its last tile may be partial, and the range end
+    // bounds both the buffer resource (rows past it load as zeros, without
+    // memory traffic) and the ids the epilogue admits.
     const int64_t nw = (int64_t)gridDim.x * WAVES;
     const int64_t gw = (int64_t)blockIdx.x * WAVES + wave;
-    const int64_t t_begin = gw * n_tiles / nw, t_end = (gw + 1) * n_tiles / nw;
+    const int64_t r_begin = gw * V / nw, r_end = (gw + 1) * V / nw;
     const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(h, M * D * 2);
 
-    int64_t t0 = t_begin;
-    for (; t0 + NT <= t_end; t0 += NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, V, t0, tk, s_w);
-    for (; t0 < t_end; ++t0) skinny2_tiles<1, KS>(hsrc, W, M, D, V, t0, tk, s_w);
+    int64_t row = r_begin;
+    for (; row + 16 * NT <= r_end; row += 16 * NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, r_end, row, tk, s_w);
+    for (; row < r_end; row += 16) skinny2_tiles<1, KS>(hsrc, W, M, D, r_end, row, tk, s_w);
 
     // workgroup list per row: the wavefronts' lists merged in groups of four
     // (a 64-lane sort each), then the groups' leaders (a 32-lane sort)
@@ -734,19 +732,28 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
 }
 
 // ---------------------------------------------------------------- merge
-// One workgroup of 10 wavefronts per row.
-// (1) The row's S sorted partial lists (S <= kMaxLists) are copied to LDS.
-// (2) Threshold selection: T = the 20th-best list head; the entries at or
-//     above T (a prefix of each list) are gathered and sorted by one
-//     wavefront.  (If there are more than 64 of them: k-way extraction, where
-//     a wavefront takes 64 lists and 20 times pops the best list head, and
-//     one wavefront then pops the best 20 of the group results.)
-// (3) Each wavefront re-scores two of those 20 exactly: all loads of the h
-//     row and both W rows are issued before any arithmetic (one HBM round
-//     trip); bf16 products are exact in float64 and summed in float64.
-// (4) Rank by the exact value (ties: lower id) and write the best 16.
+// G workgroups of 10 wavefronts per row (G = 1 for many rows, up to 5 for a
+// few, so that the exact re-scoring is spread over more CUs).
+// (1) Each copies the row's S sorted partial lists (S <= kMaxLists) to LDS.
+// (2) Threshold selection: the list heads fall into at most 64 buckets of b
+//     consecutive lists; T = the 20th-best bucket maximum.  The maxima are
+//     distinct entries, so at least 20 entries rank at or above T, and so do
+//     all of the row's best 20.  The entries at or above T (a prefix of each
+//     list, typically two dozen) are gathered and sorted in one wavefront.
+//     (More than 64 of them: k-way extraction, where a wavefront takes 64
+//     lists and 20 times pops the best list head, and one wavefront then pops
+//     the best 20 of the group results.)
+// (3) Workgroup g re-scores candidates g, g + G, ... exactly, one or two per
+//     wavefront: all loads of the h row and the W rows are issued before any
+//     arithmetic (one HBM round trip); bf16 products are exact in float64 and
+//     summed in float64.
+// (4) Rank by the exact value (ties: lower id) and write the best 16: in the
+//     same workgroup when G = 1, else in head_rank_kernel, which reads the
+//     candidates and their values from the workspace.
 constexpr int kMaxLists = 1024;
 constexpr int kMergeSeg = 10;  // 16-byte pieces per lane per pass over D
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMaxSplit = 5;  // workgroups per row at most
 
 
 
@@ -824,10 +831,28 @@ __device__ __forceinline__ void extract_top(const float* lv, const int* li, int 
     }
 }
 
+// Lane t < ns holds candidate t's exact value and id; its rank is the number
+// of candidates that rank before it (larger value, then lower id).  The best
+// 16 are written in rank order.
+__device__ __forceinline__ void rank_and_write(double z, int id, int ns, float* __restrict__ out_val,
+                                               int32_t* __restrict__ out_idx) {
+    const int lane = threadIdx.x & 63;
+    int rank = 0;
+    for (int t = 0; t < ns; ++t) {
+        const double zt = __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(z), t));
+        const int it = __builtin_amdgcn_readlane(id, t);
+        rank += ranks_before_d(zt, it, z, id) ? 1 : 0;
+    }
+    if (lane < ns && rank < kTopK) {
+        out_val[rank] = (float)z;
+        out_idx[rank] = id;
+    }
+}
+
 __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
-    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int D, int64_t V, int S,
-    const float* __restrict__ part_val, const int* __restrict__ part_idx,
-    float* __restrict__ top_val, int32_t* __restrict__ top_idx) {
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int D, int64_t V, int S, int G,
+    const float* __restrict__ part_val, const int* __restrict__ part_idx, double* __restrict__ cand_z,
+    int* __restrict__ cand_id, float* __restrict__ top_val, int32_t* __restrict__ top_idx) {
     extern __shared__ __align__(16) unsigned char smem[];
     float* lv = reinterpret_cast<float*>(smem);              // [S][16]
     int* li = reinterpret_cast<int*>(lv + (size_t)S * kTopK);  // [S][16]
@@ -836,15 +861,14 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
     __shared__ float sel_v[kRescore];
     __shared__ int sel_i[kRescore];
     __shared__ double sel_z[kRescore];
-    __shared__ unsigned long long hk[kMaxLists];             // list heads
-    __shared__ unsigned long long gh[kMaxLists / 64][32];    // per group: its 32 best heads
+    __shared__ unsigned long long bucket_max[64];
     __shared__ unsigned long long cand[64];
-    __shared__ unsigned long long s_thr;
     __shared__ int s_count;
 
-    const int64_t m = blockIdx.x;
+    const int64_t m = blockIdx.x / G;
+    const int g = blockIdx.x % G;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const float4* pv4 = reinterpret_cast<const float4*>(part_val + m * S * kTopK);
     const int4* pi4 = reinterpret_cast<const int4*>(part_idx + m * S * kTopK);
     {  // all loads of the copy are issued before any store
@@ -867,51 +891,24 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
             }
         }
     }
+    if (tid == 0) s_count = 0;
     __syncthreads();
-    // (2) T = the smallest of the kRescore largest list heads: at least
-    // kRescore entries rank at or above T, so every entry of the row's best
-    // kRescore does too.  Candidates = the entries at or above T (a prefix of
-    // each sorted list), usually a few dozen; up to 64 are sorted by one
-    // wavefront, more fall back to k-way extraction.
-    // (With fewer than kRescore lists the heads do not bound anything: T is
-    // the empty key and every entry is a candidate.)
-    if (tid == 0) {
-        s_thr = S < kRescore ? kEmptyKey : ~0ull;
-        s_count = 0;
-    }
-    for (int t = tid; t < S; t += kMergeThreads) hk[t] = rank_key(lv[t * kTopK], li[t * kTopK]);
-    __syncthreads();
-    // the 20 best heads: each group of 64 heads sorted by one wavefront, then
-    // the groups' leading 32 merged pairwise
-    const int ng = (S + 63) / 64;
-    if (S >= kRescore) {
-        for (int g = wave; g < ng; g += kMergeThreads / 64) {
-            const int t = g * 64 + lane;
-            uint64_t k = t < S ? hk[t] : kEmptyKey;
-            k = sort64_desc(k, lane);
-            if (lane < 32) gh[g][lane] = k;
-        }
+    // (2) The list heads in at most 64 buckets of b consecutive lists.
+    const int b = S <= 64 ? 1 : S <= 128 ? 2 : S <= 256 ? 4 : S <= 512 ? 8 : 16;
+    const int nb = (S + b - 1) / b;
+    for (int base = 0; base < S; base += kMergeThreads) {  // every lane takes part in the group maxima
+        const int t = base + tid;
+        uint64_t k = t < S ? rank_key(lv[t * kTopK], li[t * kTopK]) : kEmptyKey;
+        k = group_max_u64(k, b);
+        if (t < S && t % b == 0) bucket_max[t / b] = k;
     }
     __syncthreads();
-    for (int span = 1; span < ng && S >= kRescore; span <<= 1) {
-        for (int g = wave * 2 * span; g < ng; g += kMergeThreads / 64 * 2 * span) {
-            if (g + span < ng) {  // merge group g + span into group g
-                uint64_t k = lane < 32 ? gh[g][lane] : gh[g + span][63 - lane];
-                // b enters reversed (ascending) in lanes 32..63: a 64-long bitonic sequence
-                k = cx(k, xor_lane_u64<32>(k, lane), (lane & 32) == 0);
-                k = cx(k, xor_lane_u64<16>(k, lane), (lane & 16) == 0);
-                k = cx(k, xor_lane_u64<8>(k, lane), (lane & 8) == 0);
-                k = cx(k, xor_lane_u64<4>(k, lane), (lane & 4) == 0);
-                k = cx(k, xor_lane_u64<2>(k, lane), (lane & 2) == 0);
-                k = cx(k, xor_lane_u64<1>(k, lane), (lane & 1) == 0);
-                if (lane < 32) gh[g][lane] = k;
-            }
-        }
-        __syncthreads();
-    }
-    if (tid == 0 && S >= kRescore) s_thr = gh[0][kRescore - 1];
-    __syncthreads();
-    const unsigned long long T = s_thr;
+    // T = the kRescore-th best bucket maximum (every wavefront sorts the
+    // maxima itself).  With fewer than kRescore buckets there is no bound: T
+    // is the empty key and every entry is a candidate.
+    uint64_t bk = lane < nb ? bucket_max[lane] : kEmptyKey;
+    bk = sort64_desc(bk, lane);
+    const uint64_t T = nb >= kRescore ? readlane_u64(bk, kRescore - 1) : kEmptyKey;
     for (int t = tid; t < S; t += kMergeThreads) {
         for (int c = 0; c < kTopK; ++c) {
             const unsigned long long k = rank_key(lv[t * kTopK + c], li[t * kTopK + c]);
@@ -921,36 +918,37 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
         }
     }
     __syncthreads();
-    if (s_count <= 64) {
-        if (wave == 0) {
-            uint64_t k = lane < s_count ? cand[lane] : kEmptyKey;
-            k = sort64_desc(k, lane);
-            if (lane < kRescore) {
-                sel_v[lane] = key_value(k);
-                sel_i[lane] = key_id(k);
-            }
-        }
+    // lane c < kRescore of every wavefront: the c-th best candidate's key
+    uint64_t ck;
+    const int n_cand = s_count;
+    if (n_cand <= 64) {
+        ck = lane < n_cand ? cand[lane] : kEmptyKey;
+        ck = sort64_desc(ck, lane);
     } else {
-        for (int g = wave; g < ng; g += kMergeThreads / 64)
-            extract_top(lv + g * 64 * kTopK, li + g * 64 * kTopK, kTopK, min(64, S - g * 64), gv[g], gi[g]);
+        const int ng = (S + 63) / 64;
+        for (int gg = wave; gg < ng; gg += kMergeWaves)
+            extract_top(lv + gg * 64 * kTopK, li + gg * 64 * kTopK, kTopK, min(64, S - gg * 64), gv[gg], gi[gg]);
         __syncthreads();
         if (wave == 0) extract_top(&gv[0][0], &gi[0][0], kRescore, ng, sel_v, sel_i);
+        __syncthreads();
+        ck = lane < kRescore ? rank_key(sel_v[lane], sel_i[lane]) : kEmptyKey;
     }
-    __syncthreads();
-    int ns = 0;
     // real entries precede the sentinels; an id outside [0, V) (none is
     // expected) ends the list rather than being dereferenced
-    for (int c = 0; c < kRescore; ++c) {
-        if (ns == c && sel_i[c] >= 0 && sel_i[c] < V) ++ns;
-    }
+    const int cid = key_id(ck);
+    const uint64_t valid = __ballot(lane < kRescore && cid >= 0 && cid < V);
+    const int ns = __builtin_ctzll(~valid);
 
-    // exact re-scoring, two candidates per wavefront
+    // (3) exact re-scoring: candidates g, g + G, ... of this workgroup, one
+    // or two per wavefront
     const uint16_t* hr = h + m * D;
-    const int c0 = 2 * wave, c1 = 2 * wave + 1;
+    const int c0 = g + G * wave, c1 = g + G * (wave + kMergeWaves);
     if (c0 < ns) {
         const bool has1 = c1 < ns;
-        const uint16_t* w0 = W + (int64_t)sel_i[c0] * D;
-        const uint16_t* w1 = W + (int64_t)sel_i[has1 ? c1 : c0] * D;
+        const int id0 = key_id(readlane_u64(ck, c0));
+        const int id1 = has1 ? key_id(readlane_u64(ck, c1)) : id0;
+        const uint16_t* w0 = W + (int64_t)id0 * D;
+        const uint16_t* w1 = W + (int64_t)id1 * D;
         double acc0 = 0.0, acc1 = 0.0;
         for (int seg = 0; seg < D; seg += kMergeSeg * 512) {
             u32x4 ha[kMergeSeg], wa[kMergeSeg], wb[kMergeSeg];
@@ -959,7 +957,7 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
                 const int d = min(seg + (j * 64 + lane) * 8, D - 8);
                 ha[j] = *reinterpret_cast<const u32x4*>(hr + d);
                 wa[j] = *reinterpret_cast<const u32x4*>(w0 + d);
-                wb[j] = *reinterpret_cast<const u32x4*>(w1 + d);
+                if (has1) wb[j] = *reinterpret_cast<const u32x4*>(w1 + d);
             }
 #pragma unroll
             for (int j = 0; j < kMergeSeg; ++j) {
@@ -970,35 +968,55 @@ __global__ __launch_bounds__(kMergeThreads) void head_merge_kernel(
                         const double a1 = (double)bf16_to_f32(ha[j][q] >> 16);
                         acc0 = fma(a0, (double)bf16_to_f32(wa[j][q] & 0xFFFFu), acc0);
                         acc0 = fma(a1, (double)bf16_to_f32(wa[j][q] >> 16), acc0);
-                        acc1 = fma(a0, (double)bf16_to_f32(wb[j][q] & 0xFFFFu), acc1);
-                        acc1 = fma(a1, (double)bf16_to_f32(wb[j][q] >> 16), acc1);
+                        if (has1) {
+                            acc1 = fma(a0, (double)bf16_to_f32(wb[j][q] & 0xFFFFu), acc1);
+                            acc1 = fma(a1, (double)bf16_to_f32(wb[j][q] >> 16), acc1);
+                        }
                     }
                 }
             }
         }
         acc0 = wave_sum_f64(acc0);
-        acc1 = wave_sum_f64(acc1);
+        if (has1) acc1 = wave_sum_f64(acc1);
         if (lane == 63) {
-            sel_z[c0] = acc0;
-            if (has1) sel_z[c1] = acc1;
+            if (G == 1) {
+                sel_z[c0] = acc0;
+                if (has1) sel_z[c1] = acc1;
+            } else {
+                cand_z[m * kRescore + c0] = acc0;
+                if (has1) cand_z[m * kRescore + c1] = acc1;
+            }
         }
+    }
+    const int id = lane < ns ? cid : 0x7FFFFFFF;
+    if (G > 1) {  // head_rank_kernel ranks
+        if (g == 0 && wave == 0 && lane < kRescore) cand_id[m * kRescore + lane] = id;
+        return;
     }
     __syncthreads();
-    if (wave == 0) {
-        // lane t < ns holds candidate t; its rank = the candidates before it
-        const double z = lane < ns ? sel_z[lane] : 0.0;
-        const int id = lane < ns ? sel_i[lane] : 0x7FFFFFFF;
-        int rank = 0;
-        for (int t = 0; t < ns; ++t) {
-            const double zt = __shfl(z, t);
-            const int it = __shfl(id, t);
-            rank += ranks_before_d(zt, it, z, id) ? 1 : 0;
-        }
-        if (lane < ns && rank < kTopK) {
-            top_val[m * kTopK + rank] = (float)z;
-            top_idx[m * kTopK + rank] = id;
-        }
-    }
+    // (4) lane t < ns holds candidate t
+    if (wave == 0) rank_and_write(lane < ns ? sel_z[lane] : 0.0, id, ns, top_val + m * kTopK, top_idx + m * kTopK);
+}
+
+// (4) for rows merged by several workgroups: one wavefront per row reads the
+// row's candidates (ids in rank order of their float32 values, the sentinel
+// id after the last) and their exact values.
+constexpr int kRankRows = 4;  // rows per workgroup
+__global__ __launch_bounds__(64 * kRankRows) void head_rank_kernel(int64_t M, int64_t V,
+                                                                   const double* __restrict__ cand_z,
+                                                                   const int* __restrict__ cand_id,
+                                                                   float* __restrict__ top_val,
+                                                                   int32_t* __restrict__ top_idx) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * kRankRows + (threadIdx.x >> 6);
+    if (m >= M) return;
+    // both loads in one round trip (the values of entries past the last
+    // candidate are read but not used)
+    const int id = lane < kRescore ? cand_id[m * kRescore + lane] : 0x7FFFFFFF;
+    const double zr = lane < kRescore ? cand_z[m * kRescore + lane] : 0.0;
+    const uint64_t valid = __ballot(lane < kRescore && id >= 0 && id < V);
+    const int ns = __builtin_ctzll(~valid);
+    rank_and_write(lane < ns ? zr : 0.0, lane < ns ? id : 0x7FFFFFFF, ns, top_val + m * kTopK, top_idx + m * kTopK);
 }
 
 // ------------------------------------------------------------------ host
@@ -1012,6 +1030,7 @@ struct HeadPlan {
     int S;          // partial lists per row (= workgroups per M-block)
     int n_mb;
     int64_t n_tiles;
+    int G;          // merge workgroups per row
 };
 
 // One instantiation of head_wide_kernel with its launch.
@@ -1049,6 +1068,8 @@ constexpr int kCUs = 256;
 HeadPlan head_plan(int64_t M, int64_t V) {
     HeadPlan p{};
     p.n_tiles = (V + 15) / 16;
+    // merge workgroups per row: spread the re-scoring of few rows over more CUs
+    p.G = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxSplit, kCUs / M));
     if (M <= 16) {
         p.variant = kSkinny;
         p.mb_rows = 16;
@@ -1082,9 +1103,14 @@ std::once_flag g_head_attr_once;
 
 }  // namespace
 
+// Workspace: partial values [M][S][16] float, partial ids [M][S][16] int,
+// then, when rows are merged by several workgroups, the re-scored candidates:
+// exact values [M][20] double and ids [M][20] int.
 size_t head_workspace_bytes(int64_t M, int64_t V) {
     const HeadPlan p = head_plan(M, V);
-    return (size_t)M * p.S * kTopK * 8;
+    size_t b = (size_t)M * p.S * kTopK * 8;
+    if (p.G > 1) b += (size_t)M * kRescore * 12;
+    return b;
 }
 
 int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
@@ -1102,11 +1128,13 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
     const HeadPlan p = head_plan(M, V);
     float* pv = reinterpret_cast<float*>(ws);
     int* pi = reinterpret_cast<int*>(pv + (size_t)M * p.S * kTopK);
+    double* cand_z = reinterpret_cast<double*>(pi + (size_t)M * p.S * kTopK);
+    int* cand_id = reinterpret_cast<int*>(cand_z + (size_t)M * kRescore);
     switch (p.variant) {
         case kSkinny:
             hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves>), dim3(p.S),
                                dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M,
-                               D, V, p.n_tiles, pv, pi);
+                               D, V, pv, pi);
             break;
         case kWide128:
             Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
@@ -1121,8 +1149,14 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
     int st = launch_status();
     if (st != DFLASH_OK) return st;
     const size_t lds = (size_t)p.S * kTopK * 8;
-    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)M), dim3(kMergeThreads), lds, stream, h, W, D, V, p.S, pv,
-                       pi, top_val, top_idx);
+    hipLaunchKernelGGL(head_merge_kernel, dim3((unsigned)(M * p.G)), dim3(kMergeThreads), lds, stream, h, W, D, V,
+                       p.S, p.G, pv, pi, cand_z, cand_id, top_val, top_idx);
+    if (p.G > 1) {
+        st = launch_status();
+        if (st != DFLASH_OK) return st;
+        hipLaunchKernelGGL(head_rank_kernel, dim3((unsigned)((M + kRankRows - 1) / kRankRows)), dim3(64 * kRankRows),
+                           0, stream, M, V, cand_z, cand_id, top_val, top_idx);
+    }
     return launch_status();
 }
 

@@ -109,4 +109,22 @@ __device__ __forceinline__ uint64_t sort64_stage(uint64_t k, int lane) {
 }
 __device__ __forceinline__ uint64_t sort64_desc(uint64_t k, int lane) { return sort64_stage<1>(k, lane); }
 
+// The key held by lane l (l wavefront-uniform), in every lane.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Largest key over aligned groups of b consecutive lanes (b = 1, 2, 4, 8 or
+// 16, wavefront-uniform), in every lane of the group: quad permutes, then the
+// half-row and row mirrors.
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t k, int b) {
+    uint64_t p;
+    if (b >= 2) p = dpp_u64<kDppX1>(k), k = p > k ? p : k;
+    if (b >= 4) p = dpp_u64<kDppX2>(k), k = p > k ? p : k;
+    if (b >= 8) p = dpp_u64<kDppX7>(k), k = p > k ? p : k;
+    if (b >= 16) p = dpp_u64<kDppX15>(k), k = p > k ? p : k;
+    return k;
+}
+
 }  // namespace dflash

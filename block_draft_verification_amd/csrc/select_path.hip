@@ -18,9 +18,14 @@
 // float64 (each float32 product is exact in float64, so the fused
 // multiply-add rounds exactly like an add of the exact product) and writes the
 // 16x16 tile to the workspace.
-// Kernel 2 (select_dp_kernel), one wavefront per request: sixteen lanes run
-// the DP over the P positions with the back-pointers in LDS; one lane reads
-// the path back.  All DP arithmetic is float64.
+// Kernel 2 (select_dp_kernel), one workgroup per request: it reads the
+// request's tiles, values and ids into LDS in one round trip; then one
+// wavefront runs the DP over the P positions (lane j holds delta[j]; every
+// lane scans the sixteen predecessors of its column in order, with the
+// others' delta values read lane by lane) with the back-pointers in LDS, and
+// one lane reads the path back.  All DP arithmetic is float64.
+// (A single-workgroup variant that also computes the tiles was measured
+// slower: one CU then gathers every table row and forms every product.)
 
 #include "common.hpp"
 
@@ -88,56 +93,81 @@ __global__ __launch_bounds__(256) void select_pairs_kernel(const int32_t* __rest
     pairs[(((int64_t)b * n_tiles + p) * kTopK + i) * kTopK + j] = acc;
 }
 
-__global__ __launch_bounds__(64) void select_dp_kernel(const float* __restrict__ top_val,
-                                                       const int32_t* __restrict__ top_idx,
-                                                       const double* __restrict__ pairs, int P, int n_tiles,
-                                                       bool anchored, int32_t* __restrict__ path_rank,
-                                                       int32_t* __restrict__ path_tok,
-                                                       float* __restrict__ path_score) {
+// The double held by lane l (l wavefront-uniform), in every lane.
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+    const uint64_t u = (uint64_t)__double_as_longlong(x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__global__ __launch_bounds__(256) void select_dp_kernel(const float* __restrict__ top_val,
+                                                        const int32_t* __restrict__ top_idx,
+                                                        const double* __restrict__ pairs, int P, int n_tiles,
+                                                        bool anchored, int32_t* __restrict__ path_rank,
+                                                        int32_t* __restrict__ path_tok,
+                                                        float* __restrict__ path_score) {
+    __shared__ double pair_s[kMaxP][kTopK * kTopK];
     __shared__ double val_s[kMaxP][kTopK];
+    __shared__ int idx_s[kMaxP][kTopK];
     __shared__ unsigned char psi[kMaxP][kTopK];
-    __shared__ double delta[kTopK];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    for (int e = tid; e < P * kTopK; e += 64) val_s[e / kTopK][e % kTopK] = (double)top_val[(int64_t)b * P * kTopK + e];
-    const double* pb = pairs + (int64_t)b * n_tiles * kTopK * kTopK;
-    if (tid < kTopK)
-        delta[tid] = (double)top_val[(int64_t)b * P * kTopK + tid] +
-                     (anchored ? pb[(int64_t)(P - 1) * kTopK * kTopK + tid] : 0.0);
-    __syncthreads();
-    for (int p = 0; p + 1 < P; ++p) {
-        double nd = 0.0;
-        if (tid < kTopK) {
-            const int j = tid;
-            const double* pp = pb + (int64_t)p * kTopK * kTopK;
-            double best = delta[0] + pp[j];
-            int bi = 0;
-            for (int i = 1; i < kTopK; ++i) {
-                const double c = delta[i] + pp[i * kTopK + j];
-                if (c > best) {
-                    best = c;
-                    bi = i;
-                }
-            }
-            nd = val_s[p + 1][j] + best;
-            psi[p + 1][j] = (unsigned char)bi;
+    {  // one round trip: the request's tiles, values and ids
+        const double* pb = pairs + (int64_t)b * n_tiles * kTopK * kTopK;
+        double pr[kMaxP];
+#pragma unroll
+        for (int u = 0; u < kMaxP; ++u) pr[u] = u < n_tiles ? pb[u * kTopK * kTopK + tid] : 0.0;
+        const bool has = tid < P * kTopK;
+        const float v = has ? top_val[(int64_t)b * P * kTopK + tid] : 0.0f;
+        const int id = has ? top_idx[(int64_t)b * P * kTopK + tid] : 0;
+#pragma unroll
+        for (int u = 0; u < kMaxP; ++u)
+            if (u < n_tiles) pair_s[u][tid] = pr[u];
+        if (has) {
+            val_s[tid / kTopK][tid % kTopK] = (double)v;
+            idx_s[tid / kTopK][tid % kTopK] = id;
         }
-        __syncthreads();
-        if (tid < kTopK) delta[tid] = nd;
-        __syncthreads();
     }
+    __syncthreads();
+    if (tid >= 64) return;
+    // one wavefront: lane j (mod 16) holds delta[j]; every lane reads the
+    // others' values lane by lane and scans i = 0..15 in order
+    const int j = tid & 15;
+    double dl = val_s[0][j] + (anchored ? pair_s[P - 1][j] : 0.0);
+    for (int p = 0; p + 1 < P; ++p) {
+        const double* pp = pair_s[p];
+        double cv[kTopK];
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) cv[i] = pp[i * kTopK + j];
+        double best = readlane_f64(dl, 0) + cv[0];
+        int bi = 0;
+#pragma unroll
+        for (int i = 1; i < kTopK; ++i) {
+            const double c = readlane_f64(dl, i) + cv[i];
+            if (c > best) {
+                best = c;
+                bi = i;
+            }
+        }
+        if (tid < kTopK) psi[p + 1][j] = (unsigned char)bi;
+        dl = val_s[p + 1][j] + best;
+    }
+    wave_sync();
     if (tid == 0) {
         int end = 0;
-        double best = delta[0];
-        for (int i = 1; i < kTopK; ++i)
-            if (delta[i] > best) {
-                best = delta[i];
+        double best = readlane_f64(dl, 0);
+        for (int i = 1; i < kTopK; ++i) {
+            const double di = readlane_f64(dl, i);
+            if (di > best) {
+                best = di;
                 end = i;
             }
+        }
         int cur = end;
         for (int p = P - 1; p >= 0; --p) {
             path_rank[(int64_t)b * P + p] = cur;
-            path_tok[(int64_t)b * P + p] = top_idx[((int64_t)b * P + p) * kTopK + cur];
+            path_tok[(int64_t)b * P + p] = idx_s[p][cur];
             if (p > 0) cur = psi[p][cur];
         }
         path_score[b] = (float)best;
@@ -160,7 +190,7 @@ int launch_select_path(const float* top_val, const int32_t* top_idx, const int32
         const int st = launch_status();
         if (st != DFLASH_OK) return st;
     }
-    hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(64), 0, stream, top_val, top_idx, pairs, P, n_tiles,
+    hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(256), 0, stream, top_val, top_idx, pairs, P, n_tiles,
                        anchor != nullptr, path_rank, path_tok, path_score);
     return launch_status();
 }

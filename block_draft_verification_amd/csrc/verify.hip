@@ -195,9 +195,13 @@ __global__ __launch_bounds__(1024) void greedy_decide_kernel(const float2* __res
                                                              int32_t* __restrict__ out_tok,
                                                              int32_t* __restrict__ n_emit) {
     __shared__ int g[16];
+    __shared__ int d[16];
     const int b = blockIdx.x;
     const int t = threadIdx.x >> 6;
     const int l = threadIdx.x & 63;
+    const int P = T - 1;
+    // the drafts are read once, with the chunk records (one round trip)
+    if (threadIdx.x < P) d[threadIdx.x] = draft[(int64_t)b * P + threadIdx.x];
     const float2* rp = part + ((int64_t)b * T + t) * n_chunks;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
@@ -209,8 +213,6 @@ __global__ __launch_bounds__(1024) void greedy_decide_kernel(const float2* __res
     if (l == 0) g[t] = bi;
     __syncthreads();
     if (threadIdx.x == 0) {
-        const int P = T - 1;
-        const int32_t* d = draft + (int64_t)b * P;
         int32_t* o = out_tok + (int64_t)b * T;
         int n = 0;
         while (n < P && d[n] == g[n]) {
@@ -465,11 +467,6 @@ __device__ __forceinline__ uint64_t merge64_desc(uint64_t a, uint64_t b_rev, int
     return k;
 }
 
-__device__ __forceinline__ uint64_t readlane_u64(uint64_t x, int l) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), l);
-    return ((uint64_t)hi << 32) | lo;
-}
 
 // Appends this lane's keys >= thr (and non-zero) to cand[] at a workgroup
 // counter; returns nothing, the count is *count (may exceed kCandCap: then
