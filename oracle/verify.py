@@ -279,3 +279,66 @@ def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_
     if return_margins:
         return out, n_emit, margins
     return out, n_emit
+
+
+# ---------------------------------------- general (sparse) proposal q (NEXT)
+# Rejection sampling with a drawn draft (the sampled-path selector): draft
+# d = d[s-1] was proposed with probability q(d) under a distribution q that
+# is non-zero on at most K candidate ids.  Standard speculative sampling:
+# accept with probability min(1, p(d) / q(d)), i.e. iff u_acc * q(d) * Z <
+# e(d); otherwise draw from the residual max(0, p - q), renormalised.  With
+# q = one-hot(d) this is ``decide_slot``.
+
+def decide_slot_q(e, d, q_ids, q_prob, u_acc, u_res):
+    """One draft slot with proposal q (ids q_ids, probabilities q_prob; ids
+    outside the vocabulary carry no weight, repeated ids add up).  In weight
+    units the residual of token v is max(0, e(v) - q(v) * Z)."""
+    V = e.size
+    Z = float(np.sum(e))
+    qv = {}
+    for v, w in zip(q_ids, q_prob):
+        v = int(v)
+        if 0 <= v < V:
+            qv[v] = qv.get(v, 0.0) + float(w)
+    qd = qv.get(int(d), 0.0)
+    if 0 <= d < V and u_acc * qd * Z < e[d]:
+        return True, int(d)
+    resid = e.copy()
+    for v, w in qv.items():
+        resid[v] = max(0.0, e[v] - w * Z)
+    return False, inverse_cdf(resid, u_res * float(np.sum(resid)))
+
+
+def verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id, pos0):
+    """Rejection-sampling verification of drafts drawn from proposals q.
+
+    q_idx i32 [B][P][K] and q_prob f64 [B][P][K] give the proposal the draft
+    of slot s = p + 1 was drawn from.  Uniforms, rows and the bonus are those
+    of ``verify_sample``."""
+    L = f64(logits)
+    d = i64(draft)
+    qi = i64(q_idx)
+    qp = f64(q_prob)
+    rid = i64(request_id)
+    p0 = i64(pos0)
+    B, T, V = L.shape
+    P = T - 1
+    inv_tau = 1.0 / float(np.float32(temperature))
+    out = np.full((B, T), -1, dtype=np.int32)
+    n_emit = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        n = 0
+        for s in range(1, T + 1):
+            u_acc, u_res = uniforms(int(seed), int(rid[b]), int(p0[b]) + s)
+            if s <= P:
+                e = row_weights(L[b, s - 1], inv_tau)
+                accepted, tok = decide_slot_q(e, int(d[b, s - 1]), qi[b, s - 1], qp[b, s - 1], u_acc, u_res)
+                out[b, n] = tok
+                if accepted:
+                    n += 1
+                    continue
+                break
+            e = row_weights(L[b, T - 1], inv_tau)
+            out[b, n] = decide_bonus(e, u_res)
+        n_emit[b] = n + 1
+    return out, n_emit
