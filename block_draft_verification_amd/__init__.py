@@ -11,6 +11,8 @@ Entry points (same names and semantics as include/dflash.h):
     verify_greedy(logits, draft)              -> (out_tok, n_emit)
     verify_sample(logits, draft, temperature, seed, request_id, pos0)
                                               -> (out_tok, n_emit)
+and the variants select_path(..., anchor=...), select_path_sampled(...) ->
+(path_rank, path_tok, path_q), verify_sample_q(...), verify_sample_topkp(...).
 """
 
 import ctypes
@@ -38,6 +40,10 @@ _SIGNATURES = {
                                             _p, _p, _p, _psz, _p]),
     "dflash_verify_sample_topkp": (ctypes.c_int, [_p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_i32, _c_f32,
                                                   _c_u64, _p, _p, _p, _p, _p, _psz, _p]),
+    "dflash_select_path_sampled": (ctypes.c_int, [_p, _p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
+                                                  _c_u64, _p, _p, _p, _p, _p, _p, _psz, _p]),
+    "dflash_verify_sample_q": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p, _p,
+                                              _p, _p, _p, _psz, _p]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -220,6 +226,69 @@ def verify_sample(logits, draft, temperature, seed, request_id, pos0, workspace=
     return o, n
 
 
+def select_path_sampled(top_val, top_idx, F_l, F_r, seed, request_id, pos0, anchor=None, workspace=None, out=None):
+    """Sampled-path selector: top_val/top_idx/F_l/F_r as for select_path,
+    request_id/pos0 int64 [B], optional anchor int32 [B]
+    -> (path_rank i32 [B][P], path_tok i32 [B][P], path_q f64 [B][P][16])."""
+    _need(top_val, torch.float32, "top_val", 3)
+    _need(top_idx, torch.int32, "top_idx", 3)
+    _need(F_l, torch.float32, "F_l", 2)
+    _need(F_r, torch.float32, "F_r", 2)
+    _need(request_id, torch.int64, "request_id", 1)
+    _need(pos0, torch.int64, "pos0", 1)
+    B, P, K = top_val.shape
+    V, r = F_l.shape
+    if (tuple(F_r.shape) != (V, r) or tuple(top_idx.shape) != (B, P, K) or request_id.numel() != B
+            or pos0.numel() != B):
+        raise DFlashError("shape mismatch in select_path_sampled")
+    if anchor is not None:
+        _need(anchor, torch.int32, "anchor", 1)
+        if anchor.numel() != B:
+            raise DFlashError("anchor must hold one id per request")
+    if out is None:
+        rank = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
+        tok = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
+        q = torch.empty((B, P, K), dtype=torch.float64, device=top_val.device)
+    else:
+        rank, tok, q = out
+    L = lib()
+    before = (_ptr(top_val), _ptr(top_idx), None if anchor is None else _ptr(anchor), _ptr(F_l), _ptr(F_r), B, P,
+              K, V, r, int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(rank), _ptr(tok), _ptr(q))
+    ws, nbytes = _workspace(L.dflash_select_path_sampled, before, (_stream(top_val.device),), top_val.device,
+                            workspace)
+    _check(L.dflash_select_path_sampled(*before, _ptr(ws), ctypes.byref(nbytes), _stream(top_val.device)),
+           "dflash_select_path_sampled")
+    return rank, tok, q
+
+
+def verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id, pos0, workspace=None, out=None):
+    """Rejection-sampling verification of drafts drawn from proposals q:
+    q_idx int32 [B][T-1][16], q_prob float64 [B][T-1][16]; the other
+    arguments as for verify_sample."""
+    _need(logits, torch.float32, "logits", 3)
+    _need(draft, torch.int32, "draft", 2)
+    _need(q_idx, torch.int32, "q_idx", 3)
+    _need(q_prob, torch.float64, "q_prob", 3)
+    _need(request_id, torch.int64, "request_id", 1)
+    _need(pos0, torch.int64, "pos0", 1)
+    B, T, V = logits.shape
+    if (tuple(draft.shape) != (B, T - 1) or tuple(q_idx.shape) != (B, T - 1, 16)
+            or tuple(q_prob.shape) != (B, T - 1, 16) or request_id.numel() != B or pos0.numel() != B):
+        raise DFlashError("shape mismatch in verify_sample_q")
+    if out is None:
+        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
+        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
+    else:
+        o, n = out
+    L = lib()
+    before = (_ptr(logits), _ptr(draft), _ptr(q_idx), _ptr(q_prob), B, T, V, float(temperature),
+              int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
+    ws, nbytes = _workspace(L.dflash_verify_sample_q, before, (_stream(logits.device),), logits.device, workspace)
+    _check(L.dflash_verify_sample_q(*before, _ptr(ws), ctypes.byref(nbytes), _stream(logits.device)),
+           "dflash_verify_sample_q")
+    return o, n
+
+
 def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0, workspace=None,
                         out=None):
     """Rejection-sampling verification against the top-k, then top-p
@@ -324,14 +393,35 @@ def bind_verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, req
                    _ptr(workspace), ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_sample_topkp")
 
 
+def bind_select_path_sampled(top_val, top_idx, F_l, F_r, seed, request_id, pos0, rank, tok, q, workspace,
+                             anchor=None):
+    B, P, K = top_val.shape
+    V, r = F_l.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_select_path_sampled,
+                  (_ptr(top_val), _ptr(top_idx), None if anchor is None else _ptr(anchor), _ptr(F_l), _ptr(F_r), B,
+                   P, K, V, r, int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(rank), _ptr(tok), _ptr(q),
+                   _ptr(workspace), ctypes.byref(nbytes), _stream(top_val.device)), "dflash_select_path_sampled")
+
+
+def bind_verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id, pos0, out_tok, n_emit,
+                         workspace):
+    B, T, V = logits.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_verify_sample_q,
+                  (_ptr(logits), _ptr(draft), _ptr(q_idx), _ptr(q_prob), B, T, V, float(temperature),
+                   int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(out_tok), _ptr(n_emit),
+                   _ptr(workspace), ctypes.byref(nbytes), _stream(logits.device)), "dflash_verify_sample_q")
+
+
 def workspace_bytes(op, *shape_args):
     """Workspace size of an entry point for the given sizes, without a GPU call:
     op in {"head_topk": (M, D, V), "select_path": (B, P), "select_path_anchored": (B, P),
-    "verify_greedy": (B, T, V),
-    "verify_sample": (B, T, V), "verify_sample_topkp": (B, T, V, top_k)}."""
+    "select_path_sampled": (B, P, anchored), "verify_greedy": (B, T, V),
+    "verify_sample": (B, T, V), "verify_sample_q": (B, T, V), "verify_sample_topkp": (B, T, V, top_k)}."""
     L = lib()
     n = ctypes.c_size_t(0)
-    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
+    fake = [ctypes.c_void_p((i + 1) << 40) for i in range(12)]
     if op == "head_topk":
         M, D, V = shape_args
         code = L.dflash_head_topk(fake[0], fake[1], M, D, V, 16, fake[2], fake[3], None, ctypes.byref(n), None)
@@ -343,6 +433,11 @@ def workspace_bytes(op, *shape_args):
         B, P = shape_args
         code = L.dflash_select_path_anchored(fake[0], fake[1], fake[7], fake[2], fake[3], B, P, 16, 1024, 16,
                                              fake[4], fake[5], fake[6], None, ctypes.byref(n), None)
+    elif op == "select_path_sampled":
+        B, P, anchored = shape_args
+        code = L.dflash_select_path_sampled(fake[0], fake[1], fake[7] if anchored else None, fake[2], fake[3], B,
+                                            P, 16, 1024, 16, 0, fake[8], fake[9], fake[4], fake[5], fake[6], None,
+                                            ctypes.byref(n), None)
     elif op == "verify_greedy":
         B, T, V = shape_args
         code = L.dflash_verify_greedy(fake[0], fake[1], B, T, V, fake[2], fake[3], None, ctypes.byref(n), None)
@@ -350,6 +445,10 @@ def workspace_bytes(op, *shape_args):
         B, T, V = shape_args
         code = L.dflash_verify_sample(fake[0], fake[1], B, T, V, 1.0, 0, fake[4], fake[5], fake[2], fake[3],
                                       None, ctypes.byref(n), None)
+    elif op == "verify_sample_q":
+        B, T, V = shape_args
+        code = L.dflash_verify_sample_q(fake[0], fake[1], fake[8], fake[9], B, T, V, 1.0, 0, fake[4], fake[5],
+                                        fake[2], fake[3], None, ctypes.byref(n), None)
     elif op == "verify_sample_topkp":
         B, T, V, k = shape_args
         code = L.dflash_verify_sample_topkp(fake[0], fake[1], B, T, V, 1.0, k, 1.0, 0, fake[4], fake[5], fake[2],

@@ -18,13 +18,16 @@ size_t head_workspace_bytes(int64_t M, int64_t V);
 int launch_select_path(const float*, const int32_t*, const int32_t*, const float*, const float*, int, int, int64_t,
                        int, int32_t*, int32_t*, float*, void*, hipStream_t);
 size_t select_workspace_bytes(int B, int P, bool anchored);
+int launch_select_path_sampled(const float*, const int32_t*, const int32_t*, const float*, const float*, int, int,
+                               int64_t, int, uint64_t, const uint64_t*, const int64_t*, int32_t*, int32_t*, double*,
+                               void*, hipStream_t);
 size_t greedy_workspace_bytes(int B, int T, int64_t V);
 size_t sample_workspace_bytes(int B, int T, int64_t V);
 size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k);
 int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
                          hipStream_t);
-int launch_verify_sample(const float*, const int32_t*, int, int, int64_t, float, uint64_t, const uint64_t*,
-                         const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
+int launch_verify_sample(const float*, const int32_t*, const int32_t*, const double*, int, int, int64_t, float,
+                         uint64_t, const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 int launch_verify_sample_topkp(const float*, const int32_t*, int, int, int64_t, float, int, float, uint64_t,
                                const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 }  // namespace dflash
@@ -129,25 +132,38 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
     return launch_head_topk(h, W, M, D, V, top_val, top_idx, workspace, (hipStream_t)stream);
 }
 
+// Draws of the sampled-path selector (on = false: the max-sum selector).
+struct PathDraws {
+    bool on;
+    uint64_t seed;
+    const uint64_t* request_id;
+    const int64_t* pos0;
+    double* path_q;
+};
+
 static int select_common(const float* top_val, const int32_t* top_idx, const int32_t* anchor, bool anchored,
                          const float* feat_l, const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V,
-                         int32_t r, int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
-                         size_t* workspace_bytes, void* stream) {
-    if (!top_val || !top_idx || !feat_l || !feat_r || !path_rank || !path_tok || !path_score)
-        return DFLASH_ERR_INVALID;
+                         int32_t r, int32_t* path_rank, int32_t* path_tok, float* path_score, const PathDraws& dr,
+                         void* workspace, size_t* workspace_bytes, void* stream) {
+    if (!top_val || !top_idx || !feat_l || !feat_r || !path_rank || !path_tok) return DFLASH_ERR_INVALID;
+    if (dr.on ? (!dr.request_id || !dr.pos0 || !dr.path_q) : !path_score) return DFLASH_ERR_INVALID;
     if (anchored && (!anchor || !aligned4(anchor))) return DFLASH_ERR_INVALID;
     if (B < 1 || P < 1 || P > 15 || V < 1 || r < 4 || r > 256 || r % 4 != 0) return DFLASH_ERR_INVALID;
     if (K != 16) return DFLASH_ERR_UNSUPPORTED;
     if (!aligned4(top_val) || !aligned4(top_idx) || !aligned16(feat_l) || !aligned16(feat_r) ||
-        !aligned4(path_rank) || !aligned4(path_tok) || !aligned4(path_score))
+        !aligned4(path_rank) || !aligned4(path_tok))
         return DFLASH_ERR_INVALID;
-    const size_t nbp = (size_t)B * P * 4, nin = (size_t)B * P * K * 4;
-    const void* outs[3] = {path_rank, path_tok, path_score};
-    const size_t outn[3] = {nbp, nbp, (size_t)B * 4};
-    const void* ins[5] = {top_val, top_idx, feat_l, feat_r, anchor};
-    const size_t inn[5] = {nin, nin, (size_t)V * r * 4, (size_t)V * r * 4, anchored ? (size_t)B * 4 : 0};
+    if (dr.on ? (((uintptr_t)dr.request_id & 7u) || ((uintptr_t)dr.pos0 & 7u) || ((uintptr_t)dr.path_q & 7u))
+              : !aligned4(path_score))
+        return DFLASH_ERR_INVALID;
+    const size_t nbp = (size_t)B * P * 4, nin = (size_t)B * P * K * 4, n8 = (size_t)B * 8;
+    const void* outs[3] = {path_rank, path_tok, dr.on ? (const void*)dr.path_q : (const void*)path_score};
+    const size_t outn[3] = {nbp, nbp, dr.on ? (size_t)B * P * K * 8 : (size_t)B * 4};
+    const void* ins[7] = {top_val, top_idx, feat_l, feat_r, anchor, dr.request_id, dr.pos0};
+    const size_t inn[7] = {nin, nin, (size_t)V * r * 4, (size_t)V * r * 4, anchored ? (size_t)B * 4 : 0,
+                           dr.on ? n8 : 0, dr.on ? n8 : 0};
     for (int i = 0; i < 3; ++i) {
-        for (int j = 0; j < 5; ++j)
+        for (int j = 0; j < 7; ++j)
             if (overlap(outs[i], outn[i], ins[j], inn[j])) return DFLASH_ERR_INVALID;
         for (int j = i + 1; j < 3; ++j)
             if (overlap(outs[i], outn[i], outs[j], outn[j])) return DFLASH_ERR_INVALID;
@@ -156,12 +172,16 @@ static int select_common(const float* top_val, const int32_t* top_idx, const int
     int st = workspace_check(workspace, workspace_bytes, select_workspace_bytes(B, P, anchored), &query);
     if (st != DFLASH_OK || query) return st;
     const size_t nws = *workspace_bytes;
-    for (int j = 0; j < 5; ++j)
+    for (int j = 0; j < 7; ++j)
         if (overlap(workspace, nws, ins[j], inn[j])) return DFLASH_ERR_INVALID;
     for (int i = 0; i < 3; ++i)
         if (overlap(workspace, nws, outs[i], outn[i])) return DFLASH_ERR_INVALID;
     st = check_device();
     if (st != DFLASH_OK) return st;
+    if (dr.on)
+        return launch_select_path_sampled(top_val, top_idx, anchored ? anchor : nullptr, feat_l, feat_r, B, P, V, r,
+                                          dr.seed, dr.request_id, dr.pos0, path_rank, path_tok, dr.path_q, workspace,
+                                          (hipStream_t)stream);
     return launch_select_path(top_val, top_idx, anchored ? anchor : nullptr, feat_l, feat_r, B, P, V, r, path_rank,
                               path_tok, path_score, workspace, (hipStream_t)stream);
 }
@@ -171,7 +191,8 @@ int dflash_select_path(const float* top_val, const int32_t* top_idx, const float
                        int32_t* path_rank, int32_t* path_tok, float* path_score, void* workspace,
                        size_t* workspace_bytes, void* stream) {
     return select_common(top_val, top_idx, nullptr, false, feat_l, feat_r, B, P, K, V, r, path_rank, path_tok,
-                         path_score, workspace, workspace_bytes, stream);
+                         path_score, PathDraws{false, 0, nullptr, nullptr, nullptr}, workspace, workspace_bytes,
+                         stream);
 }
 
 int dflash_select_path_anchored(const float* top_val, const int32_t* top_idx, const int32_t* anchor,
@@ -179,7 +200,18 @@ int dflash_select_path_anchored(const float* top_val, const int32_t* top_idx, co
                                 int64_t V, int32_t r, int32_t* path_rank, int32_t* path_tok, float* path_score,
                                 void* workspace, size_t* workspace_bytes, void* stream) {
     return select_common(top_val, top_idx, anchor, true, feat_l, feat_r, B, P, K, V, r, path_rank, path_tok,
-                         path_score, workspace, workspace_bytes, stream);
+                         path_score, PathDraws{false, 0, nullptr, nullptr, nullptr}, workspace, workspace_bytes,
+                         stream);
+}
+
+int dflash_select_path_sampled(const float* top_val, const int32_t* top_idx, const int32_t* anchor,
+                               const float* feat_l, const float* feat_r, int32_t B, int32_t P, int32_t K, int64_t V,
+                               int32_t r, uint64_t seed, const uint64_t* request_id, const int64_t* pos0,
+                               int32_t* path_rank, int32_t* path_tok, double* path_q, void* workspace,
+                               size_t* workspace_bytes, void* stream) {
+    return select_common(top_val, top_idx, anchor, anchor != nullptr, feat_l, feat_r, B, P, K, V, r, path_rank,
+                         path_tok, nullptr, PathDraws{true, seed, request_id, pos0, path_q}, workspace,
+                         workspace_bytes, stream);
 }
 
 static int verify_common_checks(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
@@ -214,17 +246,20 @@ int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B, i
     return launch_verify_greedy(logits, draft, B, T, V, out_tok, n_emit, workspace, (hipStream_t)stream);
 }
 
-int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
-                         float temperature, uint64_t seed, const uint64_t* request_id, const int64_t* pos0,
-                         int32_t* out_tok, int32_t* n_emit, void* workspace, size_t* workspace_bytes,
-                         void* stream) {
+static int sample_common(const float* logits, const int32_t* draft, const int32_t* q_idx, const double* q_prob,
+                         bool with_q, int32_t B, int32_t T, int64_t V, float temperature, uint64_t seed,
+                         const uint64_t* request_id, const int64_t* pos0, int32_t* out_tok, int32_t* n_emit,
+                         void* workspace, size_t* workspace_bytes, void* stream) {
     int st = verify_common_checks(logits, draft, B, T, V, out_tok, n_emit);
     if (st != DFLASH_OK) return st;
     if (!request_id || !pos0 || !(temperature > 0.0f) || !isfinite(temperature)) return DFLASH_ERR_INVALID;
     if (((uintptr_t)request_id & 7u) || ((uintptr_t)pos0 & 7u)) return DFLASH_ERR_INVALID;
+    if (with_q && (!q_idx || !q_prob || !aligned4(q_idx) || ((uintptr_t)q_prob & 7u))) return DFLASH_ERR_INVALID;
     const size_t no = (size_t)B * T * 4, nn = (size_t)B * 4, n8 = (size_t)B * 8;
+    const size_t nqi = with_q ? (size_t)B * (T - 1) * 16 * 4 : 0, nqp = with_q ? (size_t)B * (T - 1) * 16 * 8 : 0;
     if (overlap(out_tok, no, request_id, n8) || overlap(out_tok, no, pos0, n8) ||
-        overlap(n_emit, nn, request_id, n8) || overlap(n_emit, nn, pos0, n8))
+        overlap(n_emit, nn, request_id, n8) || overlap(n_emit, nn, pos0, n8) || overlap(out_tok, no, q_idx, nqi) ||
+        overlap(out_tok, no, q_prob, nqp) || overlap(n_emit, nn, q_idx, nqi) || overlap(n_emit, nn, q_prob, nqp))
         return DFLASH_ERR_INVALID;
     bool query = false;
     st = workspace_check(workspace, workspace_bytes, sample_workspace_bytes(B, T, V), &query);
@@ -233,12 +268,29 @@ int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B, i
     if (overlap(workspace, nws, logits, (size_t)B * T * V * 4) ||
         overlap(workspace, nws, draft, (size_t)B * (T - 1) * 4) || overlap(workspace, nws, out_tok, no) ||
         overlap(workspace, nws, n_emit, nn) || overlap(workspace, nws, request_id, n8) ||
-        overlap(workspace, nws, pos0, n8))
+        overlap(workspace, nws, pos0, n8) || overlap(workspace, nws, q_idx, nqi) ||
+        overlap(workspace, nws, q_prob, nqp))
         return DFLASH_ERR_INVALID;
     st = check_device();
     if (st != DFLASH_OK) return st;
-    return launch_verify_sample(logits, draft, B, T, V, temperature, seed, request_id, pos0, out_tok, n_emit,
-                                workspace, (hipStream_t)stream);
+    return launch_verify_sample(logits, draft, with_q ? q_idx : nullptr, with_q ? q_prob : nullptr, B, T, V,
+                                temperature, seed, request_id, pos0, out_tok, n_emit, workspace, (hipStream_t)stream);
+}
+
+int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,
+                         float temperature, uint64_t seed, const uint64_t* request_id, const int64_t* pos0,
+                         int32_t* out_tok, int32_t* n_emit, void* workspace, size_t* workspace_bytes,
+                         void* stream) {
+    return sample_common(logits, draft, nullptr, nullptr, false, B, T, V, temperature, seed, request_id, pos0,
+                         out_tok, n_emit, workspace, workspace_bytes, stream);
+}
+
+int dflash_verify_sample_q(const float* logits, const int32_t* draft, const int32_t* q_idx, const double* q_prob,
+                           int32_t B, int32_t T, int64_t V, float temperature, uint64_t seed,
+                           const uint64_t* request_id, const int64_t* pos0, int32_t* out_tok, int32_t* n_emit,
+                           void* workspace, size_t* workspace_bytes, void* stream) {
+    return sample_common(logits, draft, q_idx, q_prob, true, B, T, V, temperature, seed, request_id, pos0, out_tok,
+                         n_emit, workspace, workspace_bytes, stream);
 }
 
 int dflash_verify_sample_topkp(const float* logits, const int32_t* draft, int32_t B, int32_t T, int64_t V,

@@ -28,6 +28,7 @@
 // slower: one CU then gathers every table row and forms every product.)
 
 #include "common.hpp"
+#include "philox.hpp"
 
 namespace dflash {
 
@@ -174,6 +175,108 @@ __global__ __launch_bounds__(256) void select_dp_kernel(const float* __restrict_
     }
 }
 
+// ---------------------------------------------------------- sampled path
+// A reading beyond the pages, which choose the path by max-sum: the draft
+// proposes a path drawn from the chain distribution whose scores the max-sum
+// selector maximises, pi(path) ~ exp(sum_p u_p(i_p) + sum_p pair_p(i_p, i_{p+1})),
+// u_p = val[p] (plus the anchor pair at p = 0).  Backward messages
+// beta_{P-1} = u_{P-1}, beta_p(i) = u_p(i) + logsumexp_j(pair_p(i, j) +
+// beta_{p+1}(j)) give the drafting-order proposals q_0 ~ exp(beta_0),
+// q_p(j) ~ exp(pair_{p-1}(i_{p-1}, j) + beta_p(j)), from which each position
+// draws with word 2 of the Philox block of the slot it fills (counter
+// (1, request_id, pos0 + p + 1, 0); the verifier uses words 0 and 1).
+// One workgroup per request: the tiles, values and ids in one round trip;
+// the backward messages with one thread per (i, j) and 16-lane reductions;
+// then one wavefront draws the positions in order (16-lane maximum and prefix
+// sums; the smallest j whose prefix sum exceeds u times the total).  All
+// float64.
+__device__ __forceinline__ double max16(double x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x = fmax(x, __shfl_xor(x, off, 16));
+    return x;
+}
+__device__ __forceinline__ double sum16(double x) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 16);
+    return x;
+}
+
+__global__ __launch_bounds__(256) void select_sample_kernel(
+    const float* __restrict__ top_val, const int32_t* __restrict__ top_idx, const double* __restrict__ pairs, int P,
+    int n_tiles, bool anchored, uint64_t seed, const uint64_t* __restrict__ request_id,
+    const int64_t* __restrict__ pos0, int32_t* __restrict__ path_rank, int32_t* __restrict__ path_tok,
+    double* __restrict__ path_q) {
+    __shared__ double pair_s[kMaxP][kTopK * kTopK];
+    __shared__ double val_s[kMaxP][kTopK];
+    __shared__ int idx_s[kMaxP][kTopK];
+    __shared__ double beta[kMaxP][kTopK];
+    __shared__ double u_s[kMaxP];
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    {  // one round trip: the request's tiles, values and ids
+        const double* pb = pairs + (int64_t)b * n_tiles * kTopK * kTopK;
+        double pr[kMaxP];
+#pragma unroll
+        for (int u = 0; u < kMaxP; ++u) pr[u] = u < n_tiles ? pb[u * kTopK * kTopK + tid] : 0.0;
+        const bool has = tid < P * kTopK;
+        const float v = has ? top_val[(int64_t)b * P * kTopK + tid] : 0.0f;
+        const int id = has ? top_idx[(int64_t)b * P * kTopK + tid] : 0;
+#pragma unroll
+        for (int u = 0; u < kMaxP; ++u)
+            if (u < n_tiles) pair_s[u][tid] = pr[u];
+        if (has) {
+            val_s[tid / kTopK][tid % kTopK] = (double)v;
+            idx_s[tid / kTopK][tid % kTopK] = id;
+        }
+    }
+    if (tid < P) {
+        const Philox4 r = philox4x64_10(1ull, request_id[b], (uint64_t)(pos0[b] + tid + 1), 0ull, seed, 0ull);
+        u_s[tid] = (double)(r.w[2] >> 11) * 0x1p-53;
+    }
+    __syncthreads();
+    auto unary = [&](int p, int i) -> double {
+        return val_s[p][i] + ((anchored && p == 0) ? pair_s[P - 1][i] : 0.0);
+    };
+    if (tid < kTopK) beta[P - 1][tid] = unary(P - 1, tid);
+    __syncthreads();
+    for (int p = P - 2; p >= 0; --p) {
+        const int i = tid >> 4, j = tid & 15;
+        const double x = pair_s[p][i * kTopK + j] + beta[p + 1][j];
+        const double mx = max16(x);
+        const double sm = sum16(exp(x - mx));
+        if (j == 0) beta[p][i] = unary(p, i) + (mx + log(sm));
+        __syncthreads();
+    }
+    if (tid >= 64) return;
+    const int j = tid & 15;
+    int prev = 0;
+    for (int p = 0; p < P; ++p) {
+        const double x = p == 0 ? beta[0][j] : pair_s[p - 1][prev * kTopK + j] + beta[p][j];
+        const double e = exp(x - max16(x));
+        double c = e;  // inclusive prefix sum over j
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const double up = __shfl_up(c, off, 16);
+            if (j >= off) c += up;
+        }
+        const double tot = __shfl(c, 15, 16);
+        const uint64_t hit = __ballot(tid < kTopK && c > u_s[p] * tot);
+        int pick;
+        if (hit) {
+            pick = __builtin_ctzll(hit);
+        } else {  // rounding left no prefix above the target: the last candidate of non-zero weight
+            const uint64_t pos = __ballot(tid < kTopK && e > 0.0);
+            pick = 63 - __builtin_clzll(pos);
+        }
+        if (tid < kTopK) path_q[((int64_t)b * P + p) * kTopK + j] = e / tot;
+        if (tid == 0) {
+            path_rank[(int64_t)b * P + p] = pick;
+            path_tok[(int64_t)b * P + p] = idx_s[p][pick];
+        }
+        prev = pick;
+    }
+}
+
 size_t select_workspace_bytes(int B, int P, bool anchored) {
     const int n_tiles = P - 1 + (anchored ? 1 : 0);
     return (size_t)B * (n_tiles > 0 ? n_tiles : 1) * kTopK * kTopK * 8;
@@ -192,6 +295,23 @@ int launch_select_path(const float* top_val, const int32_t* top_idx, const int32
     }
     hipLaunchKernelGGL(select_dp_kernel, dim3(B), dim3(256), 0, stream, top_val, top_idx, pairs, P, n_tiles,
                        anchor != nullptr, path_rank, path_tok, path_score);
+    return launch_status();
+}
+
+int launch_select_path_sampled(const float* top_val, const int32_t* top_idx, const int32_t* anchor,
+                               const float* feat_l, const float* feat_r, int B, int P, int64_t V, int r,
+                               uint64_t seed, const uint64_t* request_id, const int64_t* pos0, int32_t* path_rank,
+                               int32_t* path_tok, double* path_q, void* ws, hipStream_t stream) {
+    double* pairs = reinterpret_cast<double*>(ws);
+    const int n_tiles = P - 1 + (anchor ? 1 : 0);
+    if (n_tiles > 0) {
+        hipLaunchKernelGGL(select_pairs_kernel, dim3(n_tiles, B), dim3(256), 0, stream, top_idx, anchor, feat_l,
+                           feat_r, P, V, r, n_tiles, pairs);
+        const int st = launch_status();
+        if (st != DFLASH_OK) return st;
+    }
+    hipLaunchKernelGGL(select_sample_kernel, dim3(B), dim3(256), 0, stream, top_val, top_idx, pairs, P, n_tiles,
+                       anchor != nullptr, seed, request_id, pos0, path_rank, path_tok, path_q);
     return launch_status();
 }
 

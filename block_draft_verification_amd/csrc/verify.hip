@@ -18,6 +18,7 @@
 
 #include "common.hpp"
 #include "keysort.hpp"
+#include "philox.hpp"
 
 namespace dflash {
 
@@ -226,39 +227,6 @@ __global__ __launch_bounds__(1024) void greedy_decide_kernel(const float2* __res
 }
 
 // ================================================================ sampling
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): counter words 0 and 2 are
-// multiplied by two fixed odd constants; high/low product halves are xored with
-// words 1, 3 and the round key; the key advances by two Weyl constants.
-struct Philox4 {
-    uint64_t w[4];
-};
-
-__device__ Philox4 philox4x64_10(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
-                                 uint64_t k0, uint64_t k1) {
-    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r > 0) {
-            k0 += W0;
-            k1 += W1;
-        }
-        const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
-        const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
-        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
-        c0 = n0;
-        c1 = lo1;
-        c2 = n2;
-        c3 = lo0;
-    }
-    Philox4 out;
-    out.w[0] = c0;
-    out.w[1] = c1;
-    out.w[2] = c2;
-    out.w[3] = c3;
-    return out;
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(
     const float* __restrict__ logits, int64_t V, int n_chunks, double inv_tau,
@@ -291,13 +259,27 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(
     }
 }
 
+// Residual weights of the draft's proposal support: token id[k] weighs w[k]
+// instead of exp((l - m) * inv_tau) (ids outside the row never match).  A
+// one-hot proposal at d is the single entry (d, 0).
+struct Residual {
+    int n;
+    const int* id;     // LDS
+    const double* w;   // LDS
+    __device__ __forceinline__ double weight(int64_t v, double x) const {
+        for (int k = 0; k < n; ++k)
+            if ((int64_t)id[k] == v) x = w[k];
+        return x;
+    }
+};
+
 // Inverse CDF over a row, starting at chunk `c_start` whose preceding mass is
 // `before`: returns the smallest v >= c_start*kChunk with before + sum of
 // weights up to v > target, or -1 if the row ends first.  Weights are
-// exp((l - m) * inv_tau) with token `skip` weighted 0.
+// exp((l - m) * inv_tau), replaced by the residual weights of the support.
 __device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_chunks,
                                 int c_start, double before, double target, double m,
-                                double inv_tau, int skip, double* dscr, int* iscr) {
+                                double inv_tau, const Residual& res, double* dscr, int* iscr) {
     for (int c = c_start; c < n_chunks; ++c) {
         const int64_t e0 = (int64_t)c * kChunk + (int64_t)threadIdx.x * kPerThread;
         double w[kPerThread];
@@ -306,7 +288,7 @@ __device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t e = e0 + j;
             double x = 0.0;
-            if (e < V && (int)e != skip) x = exp(((double)row[e] - m) * inv_tau);
+            if (e < V) x = res.weight(e, exp(((double)row[e] - m) * inv_tau));
             w[j] = x;
             own += x;
         }
@@ -326,15 +308,15 @@ __device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_
     return -1;
 }
 
-// Largest v with non-zero weight (v != skip): the inverse-CDF fallback when
-// rounding leaves the target beyond the accumulated mass.
+// Largest v with non-zero weight: the inverse-CDF fallback when rounding
+// leaves the target beyond the accumulated mass.
 __device__ int last_positive(const float* __restrict__ row, int64_t V, double m, double inv_tau,
-                             int skip, int* iscr) {
+                             const Residual& res, int* iscr) {
     for (int64_t c0 = ((V - 1) / kChunk) * kChunk; c0 >= 0; c0 -= kChunk) {
         int best = -1;
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t e = c0 + (int64_t)threadIdx.x * kPerThread + j;
-            if (e < V && (int)e != skip && exp(((double)row[e] - m) * inv_tau) > 0.0) best = (int)e;
+            if (e < V && res.weight(e, exp(((double)row[e] - m) * inv_tau)) > 0.0) best = (int)e;
         }
         best = -block_min_int(-best, iscr);
         if (best >= 0) return best;
@@ -342,16 +324,30 @@ __device__ int last_positive(const float* __restrict__ row, int64_t V, double m,
     return 0;
 }
 
+// One workgroup per request decides the slots in order.  QGEN = false: the
+// draft is deterministic (q = one-hot(d)): accept iff u_acc * Z < e(d), the
+// residual is p without d.  QGEN = true: the draft of slot s was drawn from
+// the proposal q given by q_idx / q_prob [B][P][16] (ids, probabilities;
+// repeated ids add up, ids outside the vocabulary weigh nothing): accept iff
+// u_acc * q(d) * Z < e(d), the residual weight of a support token v is
+// max(0, e(v) - q(v) * Z).  With q one-hot at d both give the same numbers.
+template <bool QGEN>
 __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
-    const float* __restrict__ logits, const int32_t* __restrict__ draft,
-    const ChunkStat* __restrict__ stats, int T, int64_t V, int n_chunks, double inv_tau,
-    uint64_t seed, const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0,
+    const float* __restrict__ logits, const int32_t* __restrict__ draft, const int32_t* __restrict__ q_idx,
+    const double* __restrict__ q_prob, const ChunkStat* __restrict__ stats, int T, int64_t V, int n_chunks,
+    double inv_tau, uint64_t seed, const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0,
     int32_t* __restrict__ out_tok, int32_t* __restrict__ n_emit) {
     __shared__ double dscr[4];
     __shared__ float fscr[4];
     __shared__ int iscr[4];
     __shared__ double cum[kVerifyThreads];
     __shared__ double u_sh[2];
+    __shared__ int res_id[kTopK];      // the support's tokens (-1: no entry)
+    __shared__ double res_e[kTopK];    // their weights e(v)
+    __shared__ double res_w[kTopK];    // their residual weights
+    __shared__ int raw_id[kTopK];
+    __shared__ double raw_q[kTopK];
+    __shared__ double s_qd;
     const int b = blockIdx.x;
     const int P = T - 1;
     const uint64_t rid = request_id[b];
@@ -378,25 +374,63 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
             u_sh[0] = (double)(r.w[0] >> 11) * 0x1p-53;
             u_sh[1] = (double)(r.w[1] >> 11) * 0x1p-53;
         }
-        __syncthreads();
-        const double u_acc = u_sh[0], u_res = u_sh[1];
-        int skip = -1;
+        int n_res = 0;  // entries of the residual table
         double target;
         if (s <= P) {
             const int d = draft[(int64_t)b * P + (s - 1)];
             const bool d_ok = d >= 0 && (int64_t)d < V;  // an id outside the vocabulary has p = 0
             const double ed = d_ok ? exp(((double)row[d] - m) * inv_tau) : 0.0;
-            if (u_acc * Z < ed) {
+            if (!QGEN) {
+                if (threadIdx.x == 0) {
+                    res_id[0] = d_ok ? d : -1;
+                    res_e[0] = ed;
+                    res_w[0] = 0.0;
+                    s_qd = 1.0;
+                }
+                n_res = 1;
+            } else {
+                const int64_t qo = ((int64_t)b * P + (s - 1)) * kTopK;
+                if (threadIdx.x < kTopK) {
+                    raw_id[threadIdx.x] = q_idx[qo + threadIdx.x];
+                    raw_q[threadIdx.x] = q_prob[qo + threadIdx.x];
+                }
+                if (threadIdx.x == 0) s_qd = 0.0;
+                __syncthreads();
+                if (threadIdx.x < kTopK) {
+                    const int k = threadIdx.x, v = raw_id[k];
+                    const bool ok = v >= 0 && (int64_t)v < V;
+                    bool first = ok;
+                    double qsum = 0.0;
+                    for (int k2 = 0; k2 < kTopK; ++k2) {
+                        if (raw_id[k2] == v) {
+                            qsum += raw_q[k2];
+                            if (k2 < k) first = false;
+                        }
+                    }
+                    const double ev = first ? exp(((double)row[v] - m) * inv_tau) : 0.0;
+                    res_id[k] = first ? v : -1;
+                    res_e[k] = ev;
+                    res_w[k] = first ? fmax(0.0, ev - qsum * Z) : 0.0;
+                    if (first && v == d) s_qd = qsum;
+                }
+                n_res = kTopK;
+            }
+            __syncthreads();
+            const double u_acc = u_sh[0];
+            if (u_acc * s_qd * Z < ed) {
                 if (threadIdx.x == 0) o[n] = d;
                 ++n;
                 __syncthreads();
                 continue;
             }
-            skip = d_ok ? d : -1;
-            target = u_res * (Z - ed);
+            double adj = 0.0;
+            for (int k = 0; k < n_res; ++k) adj += res_e[k] - res_w[k];
+            target = u_sh[1] * (Z - adj);
         } else {
-            target = u_res * Z;
+            __syncthreads();
+            target = u_sh[1] * Z;
         }
+        const Residual res{n_res, res_id, res_w};
         // locate the chunk holding the target from the chunk masses
         double before = 0.0;
         int c_hit = -1;
@@ -405,7 +439,8 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
             double mass = 0.0;
             if (c < n_chunks) {
                 mass = st[c].mass * exp(((double)st[c].m - m) * inv_tau);
-                if (skip >= 0 && skip / kChunk == c) mass -= exp(((double)row[skip] - m) * inv_tau);
+                for (int k = 0; k < n_res; ++k)
+                    if (res_id[k] >= 0 && res_id[k] / kChunk == c) mass -= res_e[k] - res_w[k];
             }
             double total;
             const double excl = block_exclusive_scan(mass, dscr, total);
@@ -422,9 +457,8 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
             }
         }
         int tok = -1;
-        if (c_hit >= 0)
-            tok = inverse_cdf_from(row, V, n_chunks, c_hit, before, target, m, inv_tau, skip, dscr, iscr);
-        if (tok < 0) tok = last_positive(row, V, m, inv_tau, skip, iscr);
+        if (c_hit >= 0) tok = inverse_cdf_from(row, V, n_chunks, c_hit, before, target, m, inv_tau, res, dscr, iscr);
+        if (tok < 0) tok = last_positive(row, V, m, inv_tau, res, iscr);
         emitted = tok;
     }
     if (threadIdx.x == 0) {
@@ -819,10 +853,9 @@ int launch_verify_greedy(const float* logits, const int32_t* draft, int B, int T
     return launch_status();
 }
 
-int launch_verify_sample(const float* logits, const int32_t* draft, int B, int T, int64_t V,
-                         float temperature, uint64_t seed, const uint64_t* request_id,
-                         const int64_t* pos0, int32_t* out_tok, int32_t* n_emit, void* ws,
-                         hipStream_t stream) {
+int launch_verify_sample(const float* logits, const int32_t* draft, const int32_t* q_idx, const double* q_prob,
+                         int B, int T, int64_t V, float temperature, uint64_t seed, const uint64_t* request_id,
+                         const int64_t* pos0, int32_t* out_tok, int32_t* n_emit, void* ws, hipStream_t stream) {
     const int n_chunks = (int)((V + kChunk - 1) / kChunk);
     ChunkStat* stats = reinterpret_cast<ChunkStat*>(ws);
     const double inv_tau = 1.0 / (double)temperature;
@@ -834,8 +867,12 @@ int launch_verify_sample(const float* logits, const int32_t* draft, int B, int T
         hipLaunchKernelGGL(sample_stats_kernel<false>, grid, dim3(kVerifyThreads), 0, stream, logits, V, n_chunks, inv_tau, stats);
     int st = launch_status();
     if (st != DFLASH_OK) return st;
-    hipLaunchKernelGGL(sample_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, logits, draft, stats, T, V,
-                       n_chunks, inv_tau, seed, request_id, pos0, out_tok, n_emit);
+    if (q_idx)
+        hipLaunchKernelGGL(sample_decide_kernel<true>, dim3(B), dim3(kVerifyThreads), 0, stream, logits, draft, q_idx,
+                           q_prob, stats, T, V, n_chunks, inv_tau, seed, request_id, pos0, out_tok, n_emit);
+    else
+        hipLaunchKernelGGL(sample_decide_kernel<false>, dim3(B), dim3(kVerifyThreads), 0, stream, logits, draft,
+                           nullptr, nullptr, stats, T, V, n_chunks, inv_tau, seed, request_id, pos0, out_tok, n_emit);
     return launch_status();
 }
 

@@ -14,6 +14,10 @@
  *
  *   dflash_select_path_anchored  the selector with the block's slot-0 token as
  *                                a fixed first column
+ *   dflash_select_path_sampled   a path drawn from the lattice's chain
+ *                                distribution, with the proposals that drew it
+ *   dflash_verify_sample_q       rejection sampling of drawn drafts against a
+ *                                general (sparse) proposal
  *   dflash_verify_sample_topkp   rejection sampling against a top-k / top-p
  *                                filtered target
  *
@@ -166,6 +170,35 @@ int dflash_select_path_anchored(const float* top_val, const int32_t* top_idx,
                                 size_t* workspace_bytes, void* stream);
 
 /*
+ * Sampled-path selector.  A reading beyond the pages, which pick the path by
+ * max-sum (tamsi.dev, section "L'idee, sans le papier"): the path is drawn from
+ * the chain distribution over the same lattice,
+ *     pi(i_0..i_{P-1}) ~ exp(sum_p u_p(i_p) + sum_{p<P-1} pair_p(i_p, i_{p+1})),
+ * u_p = val[p] plus, with an anchor, pair(anchor, .) at p = 0.  With backward
+ * messages beta_{P-1} = u_{P-1}, beta_p(i) = u_p(i) + logsumexp_j(pair_p(i, j)
+ * + beta_{p+1}(j)), position p draws from its proposal given the drawn prefix,
+ *     q_0(j) ~ exp(beta_0(j)),  q_p(j) ~ exp(pair_{p-1}(i_{p-1}, j) + beta_p(j)),
+ * the smallest j whose running sum exceeds u times the total, with u from word
+ * 2 of Philox4x64-10 keyed (seed, 0) on counter (1, request_id[b],
+ * pos0[b] + p + 1, 0) (words 0 and 1 of that block are the verifier's).
+ * All float64.
+ *   anchor      i32 [B] or NULL (no anchor column)
+ *   request_id  u64 [B], pos0 i64 [B]   8-byte aligned
+ *   path_q      f64 [B][P][16]   q_p over the position's 16 candidates (given
+ *                                the drawn prefix), 8-byte aligned
+ *   other arguments as for dflash_select_path (no path_score).
+ * Requires as dflash_select_path.  Workspace as dflash_select_path, or as
+ * dflash_select_path_anchored with an anchor.
+ */
+int dflash_select_path_sampled(const float* top_val, const int32_t* top_idx,
+                               const int32_t* anchor, const float* feat_l,
+                               const float* feat_r, int32_t B, int32_t P, int32_t K,
+                               int64_t V, int32_t r, uint64_t seed,
+                               const uint64_t* request_id, const int64_t* pos0,
+                               int32_t* path_rank, int32_t* path_tok, double* path_q,
+                               void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * Greedy verification.
  * Source: tamsi.dev, section "Les chiffres qui comptent..." (greedy output is
  * exactly the target's); latenode.com, section "El desacuerdo empieza..."
@@ -208,6 +241,28 @@ int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B,
                          const uint64_t* request_id, const int64_t* pos0,
                          int32_t* out_tok, int32_t* n_emit,
                          void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification of drafts drawn from a proposal q (the
+ * output of dflash_select_path_sampled).  Standard speculative sampling: slot
+ * s accepts d = draft[b][s-1] iff u_acc * q(d) * Z_{s-1} < e_{s-1}(d)
+ * (probability min(1, p(d) / q(d))); on the first rejection it emits the
+ * smallest v whose running sum of residual weights max(0, e(v) - q(v) * Z)
+ * exceeds u_res times their total, and stops; the bonus and the uniforms are
+ * those of dflash_verify_sample.  q of slot s is the support q_idx[b][s-1][k]
+ * with probabilities q_prob[b][s-1][k], k < 16; repeated ids add up, ids
+ * outside [0, V) weigh nothing.  A one-hot q at d gives exactly
+ * dflash_verify_sample.
+ *   q_idx   i32 [B][T-1][16], q_prob f64 [B][T-1][16] (8-byte aligned)
+ *   other arguments as for dflash_verify_sample.
+ * Requires as dflash_verify_sample.  Workspace as dflash_verify_sample.
+ */
+int dflash_verify_sample_q(const float* logits, const int32_t* draft,
+                           const int32_t* q_idx, const double* q_prob, int32_t B,
+                           int32_t T, int64_t V, float temperature, uint64_t seed,
+                           const uint64_t* request_id, const int64_t* pos0,
+                           int32_t* out_tok, int32_t* n_emit,
+                           void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * Rejection-sampling verification against a filtered target.

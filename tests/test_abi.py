@@ -181,3 +181,26 @@ def test_select_anchored_validation():
     if not torch.cuda.is_available():
         n.value = 1 << 20
         assert f(*args(2, 7, 16, 4096, 192, ws=A[7])) == DEVICE
+
+
+@needs_lib
+def test_sampled_selector_and_q_verify_validation():
+    f = dfl.lib().dflash_select_path_sampled
+    n = ctypes.c_size_t(0)
+    P8 = [ctypes.c_void_p((i + 1) << 40) for i in range(12)]
+    def sel(rid=P8[8], pos0=P8[9], q=P8[6], anchor=None, K=16):
+        return f(P8[0], P8[1], anchor, P8[2], P8[3], 8, 7, K, 4096, 32, 0, rid, pos0, P8[4], P8[5], q, None,
+                 ctypes.byref(n), None)
+    assert sel() == OK and n.value == 8 * 6 * 256 * 8
+    assert sel(anchor=P8[7]) == OK and n.value == 8 * 7 * 256 * 8
+    assert sel(rid=None) == INVALID and sel(pos0=None) == INVALID and sel(q=None) == INVALID
+    assert sel(q=ctypes.c_void_p(((7) << 40) + 4)) == INVALID           # f64 output not 8-byte aligned
+    assert sel(rid=P8[4]) == INVALID                                      # request ids overlap path_rank
+    assert sel(K=8) == UNSUPPORTED
+    g = dfl.lib().dflash_verify_sample_q
+    def ver(qi=P8[8], qp=P8[9], out=P8[2]):
+        return g(P8[0], P8[1], qi, qp, 8, 8, 151936, 1.0, 0, P8[4], P8[5], out, P8[3], None, ctypes.byref(n), None)
+    assert ver() == OK and n.value >= 8 * 8 * 38 * 16
+    assert ver(qi=None) == INVALID and ver(qp=None) == INVALID
+    assert ver(qp=ctypes.c_void_p(((10) << 40) + 4)) == INVALID
+    assert ver(out=P8[8]) == INVALID                                      # out_tok overlaps q_idx
