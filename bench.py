@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--sample-top-p", type=float, default=1.0)
     ap.add_argument("--anchored", action="store_true",
                     help="selector anchored on each block's slot-0 token")
+    ap.add_argument("--sampled-path", action="store_true",
+                    help="sampled requests draw their path from the lattice's chain distribution and are "
+                         "verified against the proposals that drew it")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -102,6 +105,10 @@ class CycleRunner:
         self.ws_head = torch.empty(dfl.workspace_bytes("head_topk", cfg.M, cfg.D, cfg.V), dtype=u8, device=dev)
         self.ws_sel = torch.empty(dfl.workspace_bytes("select_path_anchored" if cfg.anchored else "select_path", B, P),
                                   dtype=u8, device=dev)
+        if cfg.sampled_path:  # the sampled requests' selector and their proposals
+            self.ws_sel_s = torch.empty(dfl.workspace_bytes("select_path_sampled", max(B - g, 1), P, cfg.anchored),
+                                        dtype=u8, device=dev)
+            self.q = torch.empty((max(B - g, 1), P, 16), dtype=torch.float64, device=dev)
         self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
         if cfg.top_k > 0:
             self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_topkp", max(B - g, 1), T, cfg.V, cfg.top_k),
@@ -119,13 +126,28 @@ class CycleRunner:
         tv3, ti3 = self.tv.view(B, cfg.P, 16), self.ti.view(B, cfg.P, 16)
         conv = [dfl.bind_conv2tap(s["x"], s["taps"], self.y_all)]
         head = dfl.bind_head_topk(s["h"], self.W, self.tv, self.ti, self.ws_head)
-        sel = dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel,
-                                   anchor=s["anchor"] if cfg.anchored else None)
+        anchor = s["anchor"] if cfg.anchored else None
+        if cfg.sampled_path and g < B:
+            sel = []
+            if g > 0:
+                sel.append(dfl.bind_select_path(tv3[:g], ti3[:g], self.F_l, self.F_r, self.rank[:g], self.tok[:g],
+                                                self.score[:g], self.ws_sel,
+                                                anchor=None if anchor is None else anchor[:g]))
+            sel.append(dfl.bind_select_path_sampled(tv3[g:], ti3[g:], self.F_l, self.F_r, cfg.seed, s["rid_s"],
+                                                    s["pos_s"], self.rank[g:], self.tok[g:], self.q, self.ws_sel_s,
+                                                    anchor=None if anchor is None else anchor[g:]))
+        else:
+            sel = [dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel,
+                                        anchor=anchor)]
         ver = []
         if g > 0:
             ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
         if g < B:
-            if cfg.top_k > 0:
+            if cfg.sampled_path:
+                ver.append(dfl.bind_verify_sample_q(s["target_s"], self.tok[g:], ti3[g:], self.q, cfg.temperature,
+                                                    cfg.seed, s["rid_s"], s["pos_s"], self.out[g:], self.n[g:],
+                                                    self.ws_s))
+            elif cfg.top_k > 0:
                 ver.append(dfl.bind_verify_sample_topkp(s["target_s"], self.tok[g:], cfg.temperature, cfg.top_k,
                                                         cfg.top_p, cfg.seed, s["rid_s"], s["pos_s"], self.out[g:],
                                                         self.n[g:], self.ws_s))
@@ -145,7 +167,8 @@ class CycleRunner:
                 for c in conv:
                     c()
                 head()
-                sel()
+                for c in sel:
+                    c()
                 for v in ver:
                     v()
             graphs.append(g)
@@ -166,7 +189,8 @@ class CycleRunner:
         head()
         if ev is not None:
             ev[2].record()
-        sel()
+        for c in sel:
+            c()
         if ev is not None:
             ev[3].record()
         for v in ver:
@@ -246,12 +270,14 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
 
     host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     t0 = time.perf_counter()
-    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored)
+    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
+              sampled_path=cfg.sampled_path)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
     while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
-        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored)
+        run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
+              sampled_path=cfg.sampled_path)
         total += time.perf_counter() - t0
         n += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -288,7 +314,11 @@ def main():
 
     dfl.lib()
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored)
+    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
+                     sampled_path=args.sampled_path)
+    if cfg.sampled_path and (cfg.top_k > 0 or cfg.verify == "greedy"):
+        print("--sampled-path needs sampled verification without a top-k / top-p filter", file=sys.stderr)
+        sys.exit(2)
     log(f"[bench] config {cfg.name}: generating inputs on {dev}")
     inp = make_cycle_inputs(cfg, device=dev)
     sets, per_set = make_sets(torch, cfg, inp, args.max_sets)
@@ -366,7 +396,8 @@ def main():
                    "hidden": cfg.D, "vocab": cfg.V, "top_k": 16, "selector_rank": cfg.r,
                    "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets),
                    **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {}),
-                   **({"selector": "anchored on slot 0"} if cfg.anchored else {})},
+                   **({"selector": "anchored on slot 0"} if cfg.anchored else {}),
+                   **({"draft_path": "sampled from the lattice (proposal q verified)"} if cfg.sampled_path else {})},
         "roofline": head_roofline(cfg, head_us),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),

@@ -28,6 +28,7 @@
 // slower: one CU then gathers every table row and forms every product.)
 
 #include "common.hpp"
+#include "keysort.hpp"
 #include "philox.hpp"
 
 namespace dflash {
@@ -188,17 +189,34 @@ __global__ __launch_bounds__(256) void select_dp_kernel(const float* __restrict_
 // One workgroup per request: the tiles, values and ids in one round trip;
 // the backward messages with one thread per (i, j) and 16-lane reductions;
 // then one wavefront draws the positions in order (16-lane maximum and prefix
-// sums; the smallest j whose prefix sum exceeds u times the total).  All
-// float64.
-__device__ __forceinline__ double max16(double x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x = fmax(x, __shfl_xor(x, off, 16));
+// sums with DPP row moves; the smallest j whose prefix sum exceeds u times the
+// total).  All float64.
+// 16-lane (one DPP row) butterflies: every lane of the row gets the result,
+// bit-identical across the row (each step adds or compares the same two
+// numbers in every lane).
+__device__ __forceinline__ double as_f64(uint64_t u) { return __longlong_as_double((long long)u); }
+__device__ __forceinline__ uint64_t as_u64(double x) { return (uint64_t)__double_as_longlong(x); }
+__device__ __forceinline__ double max16(double x, int li) {
+    x = fmax(x, as_f64(dpp_u64<kDppX1>(as_u64(x))));
+    x = fmax(x, as_f64(dpp_u64<kDppX2>(as_u64(x))));
+    x = fmax(x, as_f64(xor4_u64(as_u64(x), li)));
+    x = fmax(x, as_f64(dpp_u64<kDppX8>(as_u64(x))));
     return x;
 }
-__device__ __forceinline__ double sum16(double x) {
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, 16);
+__device__ __forceinline__ double sum16(double x, int li) {
+    x += as_f64(dpp_u64<kDppX1>(as_u64(x)));
+    x += as_f64(dpp_u64<kDppX2>(as_u64(x)));
+    x += as_f64(xor4_u64(as_u64(x), li));
+    x += as_f64(dpp_u64<kDppX8>(as_u64(x)));
     return x;
+}
+// Lane l of the row gets x of lane l - n (n = 1, 2, 4, 8), 0 below the row start.
+template <int CTRL>
+__device__ __forceinline__ double shr_row_f64(double x) {
+    const uint64_t u = as_u64(x);
+    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return as_f64(((uint64_t)hi << 32) | lo);
 }
 
 __global__ __launch_bounds__(256) void select_sample_kernel(
@@ -242,8 +260,8 @@ __global__ __launch_bounds__(256) void select_sample_kernel(
     for (int p = P - 2; p >= 0; --p) {
         const int i = tid >> 4, j = tid & 15;
         const double x = pair_s[p][i * kTopK + j] + beta[p + 1][j];
-        const double mx = max16(x);
-        const double sm = sum16(exp(x - mx));
+        const double mx = max16(x, j);
+        const double sm = sum16(exp(x - mx), j);
         if (j == 0) beta[p][i] = unary(p, i) + (mx + log(sm));
         __syncthreads();
     }
@@ -252,14 +270,13 @@ __global__ __launch_bounds__(256) void select_sample_kernel(
     int prev = 0;
     for (int p = 0; p < P; ++p) {
         const double x = p == 0 ? beta[0][j] : pair_s[p - 1][prev * kTopK + j] + beta[p][j];
-        const double e = exp(x - max16(x));
-        double c = e;  // inclusive prefix sum over j
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const double up = __shfl_up(c, off, 16);
-            if (j >= off) c += up;
-        }
-        const double tot = __shfl(c, 15, 16);
+        const double e = exp(x - max16(x, j));
+        double c = e;  // inclusive prefix sum over j (row shifts)
+        c += shr_row_f64<0x111>(c);
+        c += shr_row_f64<0x112>(c);
+        c += shr_row_f64<0x114>(c);
+        c += shr_row_f64<0x118>(c);
+        const double tot = as_f64(readlane_u64(as_u64(c), 15));
         const uint64_t hit = __ballot(tid < kTopK && c > u_s[p] * tot);
         int pick;
         if (hit) {

@@ -271,6 +271,15 @@ struct Residual {
             if ((int64_t)id[k] == v) x = w[k];
         return x;
     }
+    // bit j set: token e0 + j has an entry (j < 16)
+    __device__ __forceinline__ uint32_t mask16(int64_t e0) const {
+        uint32_t m = 0;
+        for (int k = 0; k < n; ++k) {
+            const int64_t d = (int64_t)id[k] - e0;
+            if (id[k] >= 0 && d >= 0 && d < 16) m |= 1u << d;
+        }
+        return m;
+    }
 };
 
 // Inverse CDF over a row, starting at chunk `c_start` whose preceding mass is
@@ -282,13 +291,17 @@ __device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_
                                 double inv_tau, const Residual& res, double* dscr, int* iscr) {
     for (int c = c_start; c < n_chunks; ++c) {
         const int64_t e0 = (int64_t)c * kChunk + (int64_t)threadIdx.x * kPerThread;
+        const uint32_t mask = res.mask16(e0);
         double w[kPerThread];
         double own = 0.0;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t e = e0 + j;
             double x = 0.0;
-            if (e < V) x = res.weight(e, exp(((double)row[e] - m) * inv_tau));
+            if (e < V) {
+                x = exp(((double)row[e] - m) * inv_tau);
+                if ((mask >> j) & 1u) x = res.weight(e, x);
+            }
             w[j] = x;
             own += x;
         }

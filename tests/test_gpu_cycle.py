@@ -159,3 +159,55 @@ def test_stagewise_stress_context_copy(dfl, dev):
     assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
     assert np.array_equal(res["n_emit"].cpu().numpy(), n0)
     assert res["n_emit"].float().mean().item() > 3.0
+
+
+def gpu_cycle_sampled_path(dfl, inp, cfg):
+    """The cycle with the sampled requests' path drawn (select_path_sampled)
+    and verified against its proposals (verify_sample_q)."""
+    B, T, P = cfg.B, cfg.T, cfg.P
+    tv, ti = dfl.head_topk(inp["h"], inp["W"])
+    tv3, ti3 = tv.view(B, P, 16), ti.view(B, P, 16)
+    g = {"greedy": B, "sample": 0, "mixed": B // 2}[cfg.verify]
+    tok = torch.empty((B, P), dtype=torch.int32, device=tv.device)
+    out = torch.empty((B, T), dtype=torch.int32, device=tv.device)
+    n = torch.empty((B,), dtype=torch.int32, device=tv.device)
+    if g > 0:
+        _, tok[:g], _ = dfl.select_path(tv3[:g], ti3[:g], inp["F_l"], inp["F_r"])
+        out[:g], n[:g] = dfl.verify_greedy(inp["target"][:g].contiguous(), tok[:g].contiguous())
+    rid, pos0 = inp["request_id"][g:].contiguous(), inp["pos0"][g:].contiguous()
+    _, ts, q = dfl.select_path_sampled(tv3[g:], ti3[g:], inp["F_l"], inp["F_r"], inp["seed"], rid, pos0)
+    tok[g:] = ts
+    out[g:], n[g:] = dfl.verify_sample_q(inp["target"][g:].contiguous(), ts, ti3[g:].contiguous(), q,
+                                         inp["temperature"], inp["seed"], rid, pos0)
+    torch.cuda.synchronize()
+    return {"top_idx": ti3, "top_val": tv3, "path_tok": tok, "q": q, "out_tok": out, "n_emit": n}
+
+
+def test_tiny_sampled_path_end_to_end(dfl, dev):
+    for verify, B in (("mixed", 6), ("sample", 3)):
+        cfg = get_config("c1_tiny", name=f"c1_tiny_{verify}", B=B, verify=verify, plant_alpha=3.0)
+        inp = make_cycle_inputs(cfg)
+        res = gpu_cycle_sampled_path(dfl, to_dev(inp, dev), cfg)
+        ref = run_cycle(inp, cfg.B, cfg.T, verify=verify, sampled_path=True)
+        for k in ("top_idx", "path_tok", "out_tok", "n_emit"):
+            assert np.array_equal(res[k].cpu().numpy(), ref[k]), (verify, k)
+
+
+def test_stagewise_batch8_sampled_path(dfl, dev):
+    """Batch 8 at the full shapes with the sampled path: the selector is
+    checked against the oracle fed the GPU's top-16 lists, verification
+    against the oracle fed the GPU's drafts and proposals."""
+    from oracle.selector import select_path_sampled as osel
+    from oracle.verify import verify_sample_q as oq
+    cfg = get_config("c3_b8")
+    inp = make_cycle_inputs(cfg, device=dev)
+    res = gpu_cycle_sampled_path(dfl, inp, cfg)
+    rid, pos0 = inp["request_id"].cpu(), inp["pos0"].cpu()
+    r0, t0, q0 = osel(res["top_val"].cpu().numpy(), res["top_idx"].cpu().numpy(), inp["F_l"].cpu(),
+                      inp["F_r"].cpu(), cfg.seed, rid, pos0)
+    assert np.array_equal(res["path_tok"].cpu().numpy(), t0)
+    np.testing.assert_allclose(res["q"].cpu().numpy(), q0, rtol=1e-12, atol=1e-15)
+    o0, n0 = oq(inp["target"].cpu(), res["path_tok"].cpu(), res["top_idx"].cpu(), res["q"].cpu().numpy(),
+                cfg.temperature, cfg.seed, rid, pos0)
+    assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
+    assert np.array_equal(res["n_emit"].cpu().numpy(), n0)

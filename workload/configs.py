@@ -29,6 +29,7 @@ class Config:
     top_k: int = 0            # sampled rows: 0 = full softmax, else top-k then top-p filtering
     top_p: float = 1.0
     anchored: bool = False    # selector anchored on each block's slot-0 token
+    sampled_path: bool = False  # sampled rows: the draft path is drawn (proposal q), verified against q
     K: int = 16
     L: int = 5        # conv layer calls per cycle
     seed: int = 0
