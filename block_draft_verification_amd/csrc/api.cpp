@@ -26,6 +26,7 @@ size_t sample_workspace_bytes(int B, int T, int64_t V);
 size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k);
 int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
                          hipStream_t);
+int launch_greedy_prefix(const int32_t*, const int32_t*, int, int, int32_t*, int32_t*, hipStream_t);
 int launch_verify_sample(const float*, const int32_t*, const int32_t*, const double*, int, int, int64_t, float,
                          uint64_t, const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 int launch_verify_sample_topkp(const float*, const int32_t*, int, int, int64_t, float, int, float, uint64_t,
@@ -244,6 +245,46 @@ int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B, i
     st = check_device();
     if (st != DFLASH_OK) return st;
     return launch_verify_greedy(logits, draft, B, T, V, out_tok, n_emit, workspace, (hipStream_t)stream);
+}
+
+// Workspace of the fused greedy verifier: the head's, then the target's
+// top-16 values and ids [B*T][16] (256-byte aligned offsets).
+static size_t fused_head_bytes(int64_t M, int64_t V) { return (head_workspace_bytes(M, V) + 255) / 256 * 256; }
+static size_t fused_greedy_workspace_bytes(int64_t M, int64_t V) {
+    return fused_head_bytes(M, V) + (size_t)M * 16 * 8;
+}
+
+int dflash_verify_greedy_fused(const uint16_t* h_t, const uint16_t* W, const int32_t* draft, int32_t B, int32_t T,
+                               int32_t D, int64_t V, int32_t* out_tok, int32_t* n_emit, void* workspace,
+                               size_t* workspace_bytes, void* stream) {
+    if (!h_t || !W || !draft || !out_tok || !n_emit) return DFLASH_ERR_INVALID;
+    if (B < 1 || T < 2 || T > 16 || D < 8 || D > 65536 || D % 8 != 0 || V < 16 || V >= ((int64_t)1 << 31))
+        return DFLASH_ERR_INVALID;
+    if (!aligned16(h_t) || !aligned16(W) || !aligned4(draft) || !aligned4(out_tok) || !aligned4(n_emit))
+        return DFLASH_ERR_INVALID;
+    const int64_t M = (int64_t)B * T;
+    const size_t nh = (size_t)M * D * 2, nw = (size_t)V * D * 2, nd = (size_t)B * (T - 1) * 4,
+                 no = (size_t)B * T * 4, nn = (size_t)B * 4;
+    const void* ins[3] = {h_t, W, draft};
+    const size_t inn[3] = {nh, nw, nd};
+    for (int j = 0; j < 3; ++j)
+        if (overlap(out_tok, no, ins[j], inn[j]) || overlap(n_emit, nn, ins[j], inn[j])) return DFLASH_ERR_INVALID;
+    if (overlap(out_tok, no, n_emit, nn)) return DFLASH_ERR_INVALID;
+    bool query = false;
+    int st = workspace_check(workspace, workspace_bytes, fused_greedy_workspace_bytes(M, V), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    for (int j = 0; j < 3; ++j)
+        if (overlap(workspace, nws, ins[j], inn[j])) return DFLASH_ERR_INVALID;
+    if (overlap(workspace, nws, out_tok, no) || overlap(workspace, nws, n_emit, nn)) return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
+    float* tv = reinterpret_cast<float*>(ws + fused_head_bytes(M, V));
+    int32_t* ti = reinterpret_cast<int32_t*>(tv + (size_t)M * 16);
+    st = launch_head_topk(h_t, W, M, D, V, tv, ti, ws, (hipStream_t)stream);
+    if (st != DFLASH_OK) return st;
+    return launch_greedy_prefix(ti, draft, B, T, out_tok, n_emit, (hipStream_t)stream);
 }
 
 static int sample_common(const float* logits, const int32_t* draft, const int32_t* q_idx, const double* q_prob,

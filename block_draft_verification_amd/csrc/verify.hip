@@ -226,6 +226,40 @@ __global__ __launch_bounds__(1024) void greedy_decide_kernel(const float2* __res
     }
 }
 
+// Greedy verification from the target's top-16 lists (the LM head's argmax
+// fused into its GEMM epilogue: the lists come from the head kernels, whose
+// exact re-scoring makes entry 0 the exact argmax, lowest id on ties).  One
+// wavefront per request: g[t] = top_idx[b*T + t][0], then the prefix rule.
+__global__ __launch_bounds__(64) void greedy_prefix_kernel(const int32_t* __restrict__ top_idx,
+                                                           const int32_t* __restrict__ draft, int T,
+                                                           int32_t* __restrict__ out_tok,
+                                                           int32_t* __restrict__ n_emit) {
+    __shared__ int g[16];
+    __shared__ int d[16];
+    const int b = blockIdx.x, l = threadIdx.x;
+    const int P = T - 1;
+    if (l < T) g[l] = top_idx[((int64_t)b * T + l) * kTopK];
+    if (l < P) d[l] = draft[(int64_t)b * P + l];
+    __syncthreads();
+    if (l == 0) {
+        int32_t* o = out_tok + (int64_t)b * T;
+        int n = 0;
+        while (n < P && d[n] == g[n]) {
+            o[n] = d[n];
+            ++n;
+        }
+        o[n] = g[n];
+        for (int k = n + 1; k < T; ++k) o[k] = -1;
+        n_emit[b] = n + 1;
+    }
+}
+
+int launch_greedy_prefix(const int32_t* top_idx, const int32_t* draft, int B, int T, int32_t* out_tok,
+                         int32_t* n_emit, hipStream_t stream) {
+    hipLaunchKernelGGL(greedy_prefix_kernel, dim3(B), dim3(64), 0, stream, top_idx, draft, T, out_tok, n_emit);
+    return launch_status();
+}
+
 // ================================================================ sampling
 template <bool VEC>
 __global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(

@@ -18,6 +18,8 @@
  *                                distribution, with the proposals that drew it
  *   dflash_verify_sample_q       rejection sampling of drawn drafts against a
  *                                general (sparse) proposal
+ *   dflash_verify_greedy_fused   greedy verification from target hidden states,
+ *                                the argmax taken in the LM-head GEMM epilogue
  *   dflash_verify_sample_topkp   rejection sampling against a top-k / top-p
  *                                filtered target
  *
@@ -216,6 +218,27 @@ int dflash_select_path_sampled(const float* top_val, const int32_t* top_idx,
 int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B,
                          int32_t T, int64_t V, int32_t* out_tok, int32_t* n_emit,
                          void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Greedy verification fused into the target LM head: the target's argmax per
+ * row comes out of the head GEMM's epilogue, so target logits are never
+ * written.  Source: as dflash_verify_greedy; the LM head is shared by target
+ * and draft (the selector tables are built from its rows, see
+ * dflash_select_path), so W is the draft head's matrix.
+ * g[t] = argmax_v <h_t[b*T + t], W[v]> over exact products and sums (the
+ * head's top-16 with exact re-scoring; lowest v on ties), then the prefix
+ * rule of dflash_verify_greedy.
+ *   h_t     bf16 [B*T][D]  target hidden states (row b*T + t: after slot t)
+ *   W       bf16 [V][D]    LM head
+ *   draft, out_tok, n_emit as for dflash_verify_greedy.
+ * Requires B >= 1, 2 <= T <= 16, 8 <= D <= 65536, D % 8 == 0, 16 <= V < 2^31,
+ * h_t and W 16-byte aligned.  Workspace: dflash_head_topk's for M = B*T plus
+ * B*T*16*8 bytes.
+ */
+int dflash_verify_greedy_fused(const uint16_t* h_t, const uint16_t* W,
+                               const int32_t* draft, int32_t B, int32_t T, int32_t D,
+                               int64_t V, int32_t* out_tok, int32_t* n_emit,
+                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * Rejection-sampling verification with a deterministic draft.

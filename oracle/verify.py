@@ -342,3 +342,17 @@ def verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id,
             out[b, n] = decide_bonus(e, u_res)
         n_emit[b] = n + 1
     return out, n_emit
+
+
+# ------------------------------------ greedy from target hidden states (NEXT)
+def verify_greedy_hidden(h_t, W, draft, chunk=8192):
+    """Greedy verification when the target's block logits are given by its
+    hidden states h_t [B*T][D] and the (shared) LM head W [V][D]: the logits
+    are the exact z = h_t W^T (``head.head_logits``), then ``verify_greedy``.
+    The GPU variant takes the argmax in the head GEMM's epilogue; the result
+    is defined by the logits alone."""
+    from .head import head_logits
+    d = i64(draft)
+    B, P = d.shape
+    z = head_logits(h_t, W, chunk=chunk).reshape(B, P + 1, -1)
+    return verify_greedy(z, d)

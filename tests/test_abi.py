@@ -204,3 +204,17 @@ def test_sampled_selector_and_q_verify_validation():
     assert ver(qi=None) == INVALID and ver(qp=None) == INVALID
     assert ver(qp=ctypes.c_void_p(((10) << 40) + 4)) == INVALID
     assert ver(out=P8[8]) == INVALID                                      # out_tok overlaps q_idx
+
+
+@needs_lib
+def test_greedy_fused_validation():
+    f = dfl.lib().dflash_verify_greedy_fused
+    n = ctypes.c_size_t(0)
+    P8 = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
+    def call(B=1, T=8, D=5120, V=151936, h=P8[0], out=P8[3]):
+        return f(h, P8[1], P8[2], B, T, D, V, out, P8[4], None, ctypes.byref(n), None)
+    assert call() == OK and n.value >= 1 * 8 * 512 * 16 * 8 + 8 * 16 * 8
+    assert call(T=1) == INVALID and call(T=17) == INVALID and call(D=5121) == INVALID and call(V=15) == INVALID
+    assert call(h=None) == INVALID
+    assert call(h=ctypes.c_void_p((1 << 40) + 8)) == INVALID         # h_t not 16-byte aligned
+    assert call(out=P8[2]) == INVALID                                # out_tok overlaps the drafts

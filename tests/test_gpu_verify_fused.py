@@ -1,0 +1,48 @@
+"""GPU parity of dflash_verify_greedy_fused (greedy verification with the
+target's argmax taken in the LM-head GEMM epilogue) against the oracle's
+verify_greedy on exact target logits."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle.verify import verify_greedy_hidden
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def block(seed, B, T, D, V, agree=0.8, grid=False):
+    """Target hidden states planted toward random tokens; drafts equal to
+    the target argmax with probability `agree` per slot."""
+    rng = np.random.default_rng(seed)
+    if grid:
+        W = rng.integers(-1, 2, (V, D)).astype(np.float32)
+        h = rng.integers(-1, 2, (B * T, D)).astype(np.float32)
+    else:
+        W = (0.02 * rng.standard_normal((V, D))).astype(np.float32)
+        h = rng.standard_normal((B * T, D)).astype(np.float32)
+        c = rng.integers(0, V, B * T)
+        h += (6.0 * W[c] / np.maximum((W[c] ** 2).sum(1, keepdims=True), 1e-6)).astype(np.float32)
+    return bf16(h), bf16(W), rng
+
+
+@pytest.mark.parametrize("B,T,D,V,grid", [(3, 8, 256, 4096, False), (2, 16, 512, 5000, False),
+                                          (4, 8, 64, 3001, True), (1, 8, 5120, 151936, False),
+                                          (4, 16, 5120, 20000, False)])
+def test_matches_oracle(dfl, dev, B, T, D, V, grid):
+    h, W, rng = block(B * 7 + T + V, B, T, D, V, grid=grid)
+    from oracle.head import head_logits
+    g = head_logits(h, W).reshape(B, T, V).argmax(-1)
+    d = g[:, :T - 1].copy()
+    flip = rng.random(d.shape) > 0.8
+    d[flip] = (d[flip] + 1) % V
+    draft = torch.from_numpy(d.astype(np.int32))
+    out, n = dfl.verify_greedy_fused(h.to(dev), W.to(dev), draft.to(dev))
+    torch.cuda.synchronize()
+    o0, n0 = verify_greedy_hidden(h, W, d)
+    assert np.array_equal(n.cpu().numpy(), n0)
+    assert np.array_equal(out.cpu().numpy(), o0)

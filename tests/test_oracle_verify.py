@@ -292,3 +292,38 @@ def test_topkp_unfiltered_limit_keeps_every_weighted_token():
     ids, w, Z = filtered_set(row, 1.0, 10**9, 1.0)
     assert np.array_equal(ids, np.arange(500))
     assert np.allclose(w, row_weights(row, 1.0), rtol=1e-15)
+
+
+# ------------------------------------------ greedy from target hidden states
+def test_greedy_from_hidden_states_planted_argmax():
+    """Target rows planted as s * W[c_t]: the row's logit of c_t is s |W[c_t]|^2,
+    far above every other, so g[t] = c_t by construction; drafts matching the
+    first k of them are accepted, then g[k] is emitted."""
+    from oracle.verify import verify_greedy_hidden
+    rng = np.random.default_rng(21)
+    V, D, T = 500, 256, 6
+    W = np.round(rng.standard_normal((V, D)) * 8) / 8            # exactly representable in bf16
+    c = rng.choice(V, T, replace=False)
+    h = 4.0 * W[c]                                              # one block, rows t = 0..T-1
+    for k in range(T):
+        d = c[:T - 1].copy()
+        if k < T - 1:
+            d[k] = (c[k] + 1) % V                               # first mismatch at slot k + 1
+        out, n = verify_greedy_hidden(h, W, d[None])
+        assert n[0] == k + 1
+        assert list(out[0, :k + 1]) == list(c[:k + 1])
+        assert np.all(out[0, k + 1:] == -1)
+
+
+def test_greedy_from_hidden_ties_take_the_lowest_id():
+    """Integer-grid rows where several vocabulary rows reach the maximum."""
+    from oracle.verify import verify_greedy_hidden
+    W = np.zeros((40, 8))
+    W[[7, 19, 33], 0] = 1.0                                      # three equal maxima for h = e_0
+    W[5, 1] = 1.0
+    h = np.zeros((2, 8))
+    h[:, 0] = 1.0
+    out, n = verify_greedy_hidden(h, W, np.array([[7]]))
+    assert n[0] == 2 and list(out[0]) == [7, 7]
+    out, n = verify_greedy_hidden(h, W, np.array([[19]]))
+    assert n[0] == 1 and out[0, 0] == 7
