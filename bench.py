@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--sampled-path", action="store_true",
                     help="sampled requests draw their path from the lattice's chain distribution and are "
                          "verified against the proposals that drew it")
+    ap.add_argument("--fused-target-head", action="store_true",
+                    help="greedy requests are verified from the target's hidden states through the shared LM "
+                         "head (argmax in the GEMM epilogue, no target logits)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -109,7 +112,12 @@ class CycleRunner:
             self.ws_sel_s = torch.empty(dfl.workspace_bytes("select_path_sampled", max(B - g, 1), P, cfg.anchored),
                                         dtype=u8, device=dev)
             self.q = torch.empty((max(B - g, 1), P, 16), dtype=torch.float64, device=dev)
-        self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8, device=dev)
+        if cfg.fused_target_head:
+            self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy_fused", max(g, 1), T, cfg.D, cfg.V), dtype=u8,
+                                    device=dev)
+        else:
+            self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8,
+                                    device=dev)
         if cfg.top_k > 0:
             self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_topkp", max(B - g, 1), T, cfg.V, cfg.top_k),
                                     dtype=u8, device=dev)
@@ -140,7 +148,10 @@ class CycleRunner:
             sel = [dfl.bind_select_path(tv3, ti3, self.F_l, self.F_r, self.rank, self.tok, self.score, self.ws_sel,
                                         anchor=anchor)]
         ver = []
-        if g > 0:
+        if g > 0 and cfg.fused_target_head:
+            ver.append(dfl.bind_verify_greedy_fused(s["h_target_g"], self.W, self.tok[:g], self.out[:g], self.n[:g],
+                                                    self.ws_g))
+        elif g > 0:
             ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
         if g < B:
             if cfg.sampled_path:
@@ -201,9 +212,11 @@ class CycleRunner:
 
 def make_sets(torch, cfg, inp, max_sets):
     B, g = cfg.B, {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
+    fused = cfg.fused_target_head
     base = {
         "x": inp["x"], "taps": inp["taps"], "h": inp["h"], "anchor": inp["anchor"],
-        "target_g": inp["target"][:g].contiguous() if g > 0 else None,
+        "target_g": inp["target"][:g].contiguous() if g > 0 and not fused else None,
+        "h_target_g": inp["h_target"][:g * cfg.T].contiguous() if g > 0 and fused else None,
         "target_s": inp["target"][g:].contiguous() if g < B else None,
         "rid_s": inp["request_id"][g:].contiguous(), "pos_s": inp["pos0"][g:].contiguous(),
     }
@@ -271,13 +284,13 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
     host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     t0 = time.perf_counter()
     ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
-              sampled_path=cfg.sampled_path)
+              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
     while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
         run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
-              sampled_path=cfg.sampled_path)
+              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head)
         total += time.perf_counter() - t0
         n += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -315,7 +328,10 @@ def main():
     dfl.lib()
     dev = torch.device("cuda:0")
     cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
-                     sampled_path=args.sampled_path)
+                     sampled_path=args.sampled_path, fused_target_head=args.fused_target_head)
+    if cfg.fused_target_head and cfg.verify == "sample":
+        print("--fused-target-head needs greedy requests", file=sys.stderr)
+        sys.exit(2)
     if cfg.sampled_path and (cfg.top_k > 0 or cfg.verify == "greedy"):
         print("--sampled-path needs sampled verification without a top-k / top-p filter", file=sys.stderr)
         sys.exit(2)
@@ -397,7 +413,9 @@ def main():
                    "conv_layers": cfg.L, "verify": cfg.verify, "rotating_input_sets": len(sets),
                    **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {}),
                    **({"selector": "anchored on slot 0"} if cfg.anchored else {}),
-                   **({"draft_path": "sampled from the lattice (proposal q verified)"} if cfg.sampled_path else {})},
+                   **({"draft_path": "sampled from the lattice (proposal q verified)"} if cfg.sampled_path else {}),
+                   **({"greedy_verify": "from target hidden states through the shared LM head (argmax in the "
+                                        "GEMM epilogue, no target logits)"} if cfg.fused_target_head else {})},
         "roofline": head_roofline(cfg, head_us),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),

@@ -11,7 +11,9 @@ top-p filtered target (latenode.com, FAQ: the published figures sample with
 top-p 0.95 and top-k 20); with anchored=True the selector starts from each
 block's slot-0 token; with sampled_path=True (a reading beyond the pages) the
 sampled requests draw their path from the lattice's chain distribution and are
-verified against the proposals that drew it.
+verified against the proposals that drew it; with fused_target_head=True the
+greedy requests are verified from the target's hidden states through the
+shared LM head.
 """
 
 import numpy as np
@@ -19,11 +21,12 @@ import numpy as np
 from .conv import conv2tap
 from .head import head_topk
 from .selector import select_path, select_path_sampled
-from .verify import verify_greedy, verify_sample, verify_sample_q, verify_sample_topkp
+from .verify import (verify_greedy, verify_greedy_hidden, verify_sample, verify_sample_q,
+                     verify_sample_topkp)
 
 
 def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=1.0, anchored=False,
-              sampled_path=False):
+              sampled_path=False, fused_target_head=False):
     L = inp["x"].shape[0]
     ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
     vals, idx, _ = head_topk(inp["h"], inp["W"], K=K, chunk=head_chunk)
@@ -48,7 +51,9 @@ def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=
     logits = inp["target"]
     out = np.full((B, T), -1, np.int32)
     n = np.zeros(B, np.int32)
-    if g > 0:
+    if g > 0 and fused_target_head:
+        out[:g], n[:g] = verify_greedy_hidden(inp["h_target"][:g * T], inp["W"], tok[:g], chunk=head_chunk)
+    elif g > 0:
         out[:g], n[:g] = verify_greedy(logits[:g], tok[:g])
     if g < B and sampled_path:
         out[g:], n[g:] = verify_sample_q(logits[g:], tok[g:], idx[g:], q, inp["temperature"], inp["seed"],

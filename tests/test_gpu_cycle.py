@@ -211,3 +211,25 @@ def test_stagewise_batch8_sampled_path(dfl, dev):
                 cfg.temperature, cfg.seed, rid, pos0)
     assert np.array_equal(res["out_tok"].cpu().numpy(), o0)
     assert np.array_equal(res["n_emit"].cpu().numpy(), n0)
+
+
+def test_fused_target_head_cycle(dfl, dev):
+    """Greedy verification from target hidden states through the shared LM
+    head (argmax in the GEMM epilogue) inside a cycle, on reduced shapes of
+    the batch-1 and stress workloads, against the oracle cycle."""
+    for name, kw in (("c2_b1", dict(name="c2_fused", B=3, D=1024, V=8192)),
+                     ("c5_stress", dict(name="c5_fused", B=4, D=1024, V=8192)),
+                     ("c4_b32", dict(name="c4_fused", B=6, D=512, V=4000))):
+        cfg = get_config(name, **kw)
+        inp = make_cycle_inputs(cfg)
+        d = to_dev(inp, dev)
+        B, T, P = cfg.B, cfg.T, cfg.P
+        tv, ti = dfl.head_topk(d["h"], d["W"])
+        _, tok, _ = dfl.select_path(tv.view(B, P, 16), ti.view(B, P, 16), d["F_l"], d["F_r"])
+        g = {"greedy": B, "sample": 0, "mixed": B // 2}[cfg.verify]
+        out, n = dfl.verify_greedy_fused(d["h_target"][:g * T].contiguous(), d["W"], tok[:g].contiguous())
+        torch.cuda.synchronize()
+        ref = run_cycle(inp, B, T, verify=cfg.verify, fused_target_head=True)
+        assert np.array_equal(tok.cpu().numpy(), ref["path_tok"]), name
+        assert np.array_equal(out.cpu().numpy(), ref["out_tok"][:g]), name
+        assert np.array_equal(n.cpu().numpy(), ref["n_emit"][:g]), name

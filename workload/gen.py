@@ -20,6 +20,14 @@ float32 and rounded to nearest-even):
     round(agree_frac * B * (T-1)) seeded (request, slot) pairs the planted
     draft token is raised to the row maximum + 1, and on the others it is
     pushed 1 below the best other token when it happened to be the argmax.
+* target hidden states h_target [B*T][D] bf16, the same block in hidden
+  space (for greedy verification fused into the shared LM head):
+  - "draft_plus_noise": row t < T-1 is draft hidden t plus N(0, s^2) with
+    s = noise_sd / (w_sd sqrt(D)), so that its logits carry noise of about
+    noise_sd; row T-1 is the fresh hidden plus the same noise;
+  - "context_copy": rows ~ N(0, 1) planted (plant_alpha) toward the draft's
+    planted token on the agreeing (request, slot) pairs and toward another
+    random token on the others; row T-1 ~ N(0, 1).
 * request ids 0..B-1 (uint64 semantics), anchor positions 4096 + 64 b.
 
 Every tensor has its own generator, seeded from (seed, config name, tensor
@@ -111,6 +119,9 @@ def make_cycle_inputs(cfg, device="cpu"):
             rows = torch.cat([hb[b], fresh[b:b + 1]], dim=0)  # [T][D]
             target[b] = _rows_times_wt(rows, W)
             target[b] += _randn((T, V), noise, dev, cfg.noise_sd)
+        sd_h = cfg.noise_sd / (cfg.w_sd * float(np.sqrt(D)))
+        ht_rows = hb + _randn((B, P, D), gen("h_target_noise"), dev, sd_h)
+        ht_bonus = fresh + _randn((B, D), gen("h_target_bonus"), dev, sd_h)
     elif cfg.logits == "context_copy":
         sd = float(np.sqrt(cfg.w_sd ** 2 * D + 1.0))
         g = gen("target")
@@ -130,6 +141,12 @@ def make_cycle_inputs(cfg, device="cpu"):
             elif int(torch.argmax(row)) == c:
                 row[c] = -float("inf")
                 row[c] = row.max() - 1.0
+        ht_rows = _randn((B * P, D), gen("h_target"), dev)
+        alt = torch.randint(0, V, (B * P,), generator=gen("h_target_alt"), device=dev, dtype=torch.int64)
+        toward = torch.where(agree.to(dev), planted, alt)
+        wt = W[toward].float()
+        ht_rows = (ht_rows + cfg.plant_alpha * wt / (wt * wt).sum(dim=1, keepdim=True)).view(B, P, D)
+        ht_bonus = _randn((B, D), gen("h_target_bonus"), dev)
     else:
         raise ValueError(cfg.logits)
 
@@ -138,9 +155,10 @@ def make_cycle_inputs(cfg, device="cpu"):
     anchor = torch.randint(0, V, (B,), generator=gen("anchor"), device=dev, dtype=torch.int64).to(torch.int32)
     request_id = torch.arange(B, dtype=torch.int64, device=dev)
     pos0 = 4096 + 64 * torch.arange(B, dtype=torch.int64, device=dev)
+    h_target = torch.cat([ht_rows, ht_bonus.view(B, 1, D)], dim=1).reshape(B * T, D).to(torch.bfloat16)
     return {
         "x": x, "taps": taps, "h": h, "W": W, "F_l": F_l, "F_r": F_r,
-        "target": target, "request_id": request_id, "pos0": pos0, "anchor": anchor,
+        "target": target, "h_target": h_target, "request_id": request_id, "pos0": pos0, "anchor": anchor,
         "planted": planted, "temperature": float(cfg.temperature),
         "seed": int(cfg.seed),
     }
