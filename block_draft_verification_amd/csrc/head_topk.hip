@@ -1022,7 +1022,7 @@ __global__ __launch_bounds__(64 * kRankRows) void head_rank_kernel(int64_t M, in
 // ------------------------------------------------------------------ host
 namespace {
 
-enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3 };
+enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3, kWide64 = 4 };
 
 struct HeadPlan {
     HeadVariant variant;
@@ -1063,6 +1063,10 @@ using Wide224 = WideVariant<7, 2, 2, 2, true, 4>;  // M-blocks of 224 rows
 // several 128-row M-blocks (MFMA-bound sizes): 256-row strips in unpadded,
 // swizzled tiles, half the fragment reads per MFMA (M = 480: 1383 -> 1225 us)
 using Wide128W = WideVariant<4, 4, 2, 2, true, 4, true>;
+// at most 64 rows: 64-row blocks keep both wavefront rows busy (M = 56:
+// 306 us against 321 us with a 128-row block, whose second wavefront row
+// holds no rows; 256-row strips and deeper prefetch measured slower)
+using Wide64 = WideVariant<2, 2, 2, 4, true, 4>;
 constexpr int kCUs = 256;
 
 HeadPlan head_plan(int64_t M, int64_t V) {
@@ -1087,6 +1091,9 @@ HeadPlan head_plan(int64_t M, int64_t V) {
     } else if (M > 128) {
         p.variant = kWide128W;
         p.mb_rows = Wide128W::Cfg::MB;
+    } else if (M <= 64) {
+        p.variant = kWide64;
+        p.mb_rows = Wide64::Cfg::MB;
     } else {
         p.variant = kWide128;
         p.mb_rows = Wide128::Cfg::MB;
@@ -1122,6 +1129,7 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
         Wide128::set_attr();
         Wide224::set_attr();
         Wide128W::set_attr();
+        Wide64::set_attr();
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLists * kTopK * 8);
     });
@@ -1138,6 +1146,9 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
             break;
         case kWide128:
             Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            break;
+        case kWide64:
+            Wide64::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
         case kWide128W:
             Wide128W::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
