@@ -253,6 +253,29 @@ def head_roofline(cfg, head_us):
             "hbm_frac": round(bytes_ / t / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def cycle_roofline(cfg, ms_cycle):
+    fl = cycle_floor(cfg)
+    floor_us = sum(fl.values())
+    return {"floor_us": round(floor_us, 2), "measured_us": round(ms_cycle * 1e3, 2),
+            "frac": round(floor_us / (ms_cycle * 1e3), 4), "floor_us_by_step": {k: round(v, 2) for k, v in fl.items()},
+            "note": "sum of the steps' roofline floors (HBM 8 TB/s; the head at max(bytes, bf16 MFMA 2.5 PFLOP/s)) "
+                    "over the measured cycle; the logits-based cycle (target head not included)"}
+
+
+def cycle_floor(cfg):
+    """Roofline floor of one cycle: every step's algorithmic bytes at the HBM
+    peak, the head at the larger of its byte and MFMA times.  conv: x, both
+    taps and y per token; head: W once, h, the lists; selector: the table rows
+    it gathers; verify: the target logits once."""
+    hbm = HBM_PEAK_GBS * 1e9
+    conv = 8.0 * cfg.L * cfg.B * cfg.T * cfg.D / hbm
+    head_bytes = cfg.V * cfg.D * 2 + cfg.M * cfg.D * 2 + cfg.M * 16 * 8
+    head = max(head_bytes / hbm, 2.0 * cfg.M * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    sel = cfg.B * max(cfg.P - 1, 0) * 2 * 16 * cfg.r * 4 / hbm
+    ver = 4.0 * cfg.B * cfg.T * cfg.V / hbm
+    return {"conv": conv * 1e6, "head_topk": head * 1e6, "select_path": sel * 1e6, "verify": ver * 1e6}
+
+
 def head_source_sha():
     h = hashlib.sha256()
     for path in HEAD_SRC:
@@ -417,6 +440,7 @@ def main():
                    **({"greedy_verify": "from target hidden states through the shared LM head (argmax in the "
                                         "GEMM epilogue, no target logits)"} if cfg.fused_target_head else {})},
         "roofline": head_roofline(cfg, head_us),
+        "cycle_roofline": cycle_roofline(cfg, ms_graph),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),
                       "select_path": round(float(np.median(stage[:, 2])), 2),
