@@ -259,7 +259,7 @@ def cycle_roofline(cfg, ms_cycle):
     return {"floor_us": round(floor_us, 2), "measured_us": round(ms_cycle * 1e3, 2),
             "frac": round(floor_us / (ms_cycle * 1e3), 4), "floor_us_by_step": {k: round(v, 2) for k, v in fl.items()},
             "note": "sum of the steps' roofline floors (HBM 8 TB/s; the head at max(bytes, bf16 MFMA 2.5 PFLOP/s)) "
-                    "over the measured cycle; the logits-based cycle (target head not included)"}
+                    "over the measured cycle"}
 
 
 def cycle_floor(cfg):
@@ -272,7 +272,13 @@ def cycle_floor(cfg):
     head_bytes = cfg.V * cfg.D * 2 + cfg.M * cfg.D * 2 + cfg.M * 16 * 8
     head = max(head_bytes / hbm, 2.0 * cfg.M * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     sel = cfg.B * max(cfg.P - 1, 0) * 2 * 16 * cfg.r * 4 / hbm
-    ver = 4.0 * cfg.B * cfg.T * cfg.V / hbm
+    g = {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
+    if cfg.fused_target_head:  # the greedy requests' target head instead of their logits
+        mt = g * cfg.T
+        ver = max((cfg.V * cfg.D * 2 + mt * cfg.D * 2) / hbm, 2.0 * mt * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+        ver += 4.0 * (cfg.B - g) * cfg.T * cfg.V / hbm
+    else:
+        ver = 4.0 * cfg.B * cfg.T * cfg.V / hbm
     return {"conv": conv * 1e6, "head_topk": head * 1e6, "select_path": sel * 1e6, "verify": ver * 1e6}
 
 
