@@ -356,3 +356,17 @@ def verify_greedy_hidden(h_t, W, draft, chunk=8192):
     B, P = d.shape
     z = head_logits(h_t, W, chunk=chunk).reshape(B, P + 1, -1)
     return verify_greedy(z, d)
+
+
+def verify_sample_hidden(h_t, W, draft, temperature, seed, request_id, pos0, chunk=8192, return_margins=False):
+    """Rejection-sampling verification when the target's block logits are
+    given by its hidden states h_t [B*T][D] and the shared LM head W [V][D]:
+    the exact logits z = h_t W^T (``head.head_logits``), then ``verify_sample``.
+    The GPU variant takes the row statistics in the head GEMM's epilogue from
+    float32 logits; its decisions can differ from these only when a uniform
+    falls within the float32 error of a decision boundary (see the margins)."""
+    from .head import head_logits
+    d = i64(draft)
+    B, P = d.shape
+    z = head_logits(h_t, W, chunk=chunk).reshape(B, P + 1, -1)
+    return verify_sample(z, d, temperature, seed, request_id, pos0, return_margins=return_margins)

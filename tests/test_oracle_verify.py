@@ -327,3 +327,20 @@ def test_greedy_from_hidden_ties_take_the_lowest_id():
     assert n[0] == 2 and list(out[0]) == [7, 7]
     out, n = verify_greedy_hidden(h, W, np.array([[19]]))
     assert n[0] == 1 and out[0, 0] == 7
+
+
+def test_sample_from_hidden_states_equals_sampling_integer_logits():
+    """Integer-grid hidden states and head rows: the logits are integers,
+    computed here by an int64 matrix product, and the hidden-state sampler
+    must decide exactly as the sampler given those logits."""
+    from oracle.verify import verify_sample_hidden
+    rng = np.random.default_rng(23)
+    B, T, V, D = 6, 5, 300, 32
+    W = rng.integers(-2, 3, (V, D))
+    h = rng.integers(-2, 3, (B * T, D))
+    z = (h.astype(np.int64) @ W.astype(np.int64).T).reshape(B, T, V)
+    d = np.argsort(-z[:, :T - 1], axis=-1, kind="stable")[..., 1]   # second-best tokens as drafts
+    rid, pos0 = np.arange(B) * 5 + 2, np.full(B, 40)
+    ref = verify_sample(z.astype(np.float64) * 0.25, d, 1.0, 8, rid, pos0)
+    got = verify_sample_hidden(h * 0.5, W * 0.5, d, 1.0, 8, rid, pos0)
+    assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
