@@ -46,6 +46,8 @@ _SIGNATURES = {
                                               _p, _p, _p, _psz, _p]),
     "dflash_verify_greedy_fused": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _p, _p, _p, _psz,
                                                   _p]),
+    "dflash_verify_sample_fused": (ctypes.c_int, [_p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_f32, _c_u64, _p,
+                                                  _p, _p, _p, _p, _psz, _p]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -317,6 +319,36 @@ def verify_greedy_fused(h_t, W, draft, workspace=None, out=None):
     return o, n
 
 
+def verify_sample_fused(h_t, W, draft, temperature, seed, request_id, pos0, workspace=None, out=None):
+    """Rejection-sampling verification from target hidden states h_t bf16
+    [B*T][D] through the LM head W bf16 [V][D] (softmax statistics in the head
+    GEMM's epilogue; logits are never written); the other arguments as for
+    verify_sample."""
+    _need(h_t, torch.bfloat16, "h_t", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(draft, torch.int32, "draft", 2)
+    _need(request_id, torch.int64, "request_id", 1)
+    _need(pos0, torch.int64, "pos0", 1)
+    B, P = draft.shape
+    T = P + 1
+    M, D = h_t.shape
+    V = W.shape[0]
+    if M != B * T or W.shape[1] != D or request_id.numel() != B or pos0.numel() != B:
+        raise DFlashError("shape mismatch in verify_sample_fused")
+    if out is None:
+        o = torch.empty((B, T), dtype=torch.int32, device=h_t.device)
+        n = torch.empty((B,), dtype=torch.int32, device=h_t.device)
+    else:
+        o, n = out
+    L = lib()
+    before = (_ptr(h_t), _ptr(W), _ptr(draft), B, T, D, V, float(temperature), int(seed) & (2**64 - 1),
+              _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
+    ws, nbytes = _workspace(L.dflash_verify_sample_fused, before, (_stream(h_t.device),), h_t.device, workspace)
+    _check(L.dflash_verify_sample_fused(*before, _ptr(ws), ctypes.byref(nbytes), _stream(h_t.device)),
+           "dflash_verify_sample_fused")
+    return o, n
+
+
 def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0, workspace=None,
                         out=None):
     """Rejection-sampling verification against the top-k, then top-p
@@ -450,10 +482,20 @@ def bind_verify_greedy_fused(h_t, W, draft, out_tok, n_emit, workspace):
                    _ptr(workspace), ctypes.byref(nbytes), _stream(h_t.device)), "dflash_verify_greedy_fused")
 
 
+def bind_verify_sample_fused(h_t, W, draft, temperature, seed, request_id, pos0, out_tok, n_emit, workspace):
+    B, P = draft.shape
+    nbytes = ctypes.c_size_t(workspace.numel())
+    return _bound(lib().dflash_verify_sample_fused,
+                  (_ptr(h_t), _ptr(W), _ptr(draft), B, P + 1, h_t.shape[1], W.shape[0], float(temperature),
+                   int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(out_tok), _ptr(n_emit),
+                   _ptr(workspace), ctypes.byref(nbytes), _stream(h_t.device)), "dflash_verify_sample_fused")
+
+
 def workspace_bytes(op, *shape_args):
     """Workspace size of an entry point for the given sizes, without a GPU call:
     op in {"head_topk": (M, D, V), "select_path": (B, P), "select_path_anchored": (B, P),
     "select_path_sampled": (B, P, anchored), "verify_greedy": (B, T, V), "verify_greedy_fused": (B, T, D, V),
+    "verify_sample_fused": (B, T, D, V),
     "verify_sample": (B, T, V), "verify_sample_q": (B, T, V), "verify_sample_topkp": (B, T, V, top_k)}."""
     L = lib()
     n = ctypes.c_size_t(0)
@@ -478,6 +520,10 @@ def workspace_bytes(op, *shape_args):
         B, T, D, V = shape_args
         code = L.dflash_verify_greedy_fused(fake[0], fake[1], fake[2], B, T, D, V, fake[3], fake[4], None,
                                             ctypes.byref(n), None)
+    elif op == "verify_sample_fused":
+        B, T, D, V = shape_args
+        code = L.dflash_verify_sample_fused(fake[0], fake[1], fake[2], B, T, D, V, 1.0, 0, fake[5], fake[6],
+                                            fake[3], fake[4], None, ctypes.byref(n), None)
     elif op == "verify_greedy":
         B, T, V = shape_args
         code = L.dflash_verify_greedy(fake[0], fake[1], B, T, V, fake[2], fake[3], None, ctypes.byref(n), None)

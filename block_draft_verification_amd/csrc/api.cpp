@@ -27,6 +27,9 @@ size_t sample_topkp_workspace_bytes(int B, int T, int64_t V, int top_k);
 int launch_verify_greedy(const float*, const int32_t*, int, int, int64_t, int32_t*, int32_t*, void*,
                          hipStream_t);
 int launch_greedy_prefix(const int32_t*, const int32_t*, int, int, int32_t*, int32_t*, hipStream_t);
+size_t sample_hidden_workspace_bytes(int B, int T, int64_t V);
+int launch_verify_sample_hidden(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, int64_t, float,
+                                uint64_t, const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 int launch_verify_sample(const float*, const int32_t*, const int32_t*, const double*, int, int, int64_t, float,
                          uint64_t, const uint64_t*, const int64_t*, int32_t*, int32_t*, void*, hipStream_t);
 int launch_verify_sample_topkp(const float*, const int32_t*, int, int, int64_t, float, int, float, uint64_t,
@@ -285,6 +288,37 @@ int dflash_verify_greedy_fused(const uint16_t* h_t, const uint16_t* W, const int
     st = launch_head_topk(h_t, W, M, D, V, tv, ti, ws, (hipStream_t)stream);
     if (st != DFLASH_OK) return st;
     return launch_greedy_prefix(ti, draft, B, T, out_tok, n_emit, (hipStream_t)stream);
+}
+
+int dflash_verify_sample_fused(const uint16_t* h_t, const uint16_t* W, const int32_t* draft, int32_t B, int32_t T,
+                               int32_t D, int64_t V, float temperature, uint64_t seed, const uint64_t* request_id,
+                               const int64_t* pos0, int32_t* out_tok, int32_t* n_emit, void* workspace,
+                               size_t* workspace_bytes, void* stream) {
+    if (!h_t || !W || !draft || !out_tok || !n_emit || !request_id || !pos0) return DFLASH_ERR_INVALID;
+    if (B < 1 || T < 2 || T > 16 || D < 8 || D > 65536 || D % 8 != 0 || V < 16 || V >= ((int64_t)1 << 31))
+        return DFLASH_ERR_INVALID;
+    if (!(temperature > 0.0f) || !isfinite(temperature)) return DFLASH_ERR_INVALID;
+    if (!aligned16(h_t) || !aligned16(W) || !aligned4(draft) || !aligned4(out_tok) || !aligned4(n_emit) ||
+        ((uintptr_t)request_id & 7u) || ((uintptr_t)pos0 & 7u))
+        return DFLASH_ERR_INVALID;
+    const int64_t M = (int64_t)B * T;
+    const size_t no = (size_t)B * T * 4, nn = (size_t)B * 4, n8 = (size_t)B * 8;
+    const void* ins[5] = {h_t, W, draft, request_id, pos0};
+    const size_t inn[5] = {(size_t)M * D * 2, (size_t)V * D * 2, (size_t)B * (T - 1) * 4, n8, n8};
+    for (int j = 0; j < 5; ++j)
+        if (overlap(out_tok, no, ins[j], inn[j]) || overlap(n_emit, nn, ins[j], inn[j])) return DFLASH_ERR_INVALID;
+    if (overlap(out_tok, no, n_emit, nn)) return DFLASH_ERR_INVALID;
+    bool query = false;
+    int st = workspace_check(workspace, workspace_bytes, sample_hidden_workspace_bytes(B, T, V), &query);
+    if (st != DFLASH_OK || query) return st;
+    const size_t nws = *workspace_bytes;
+    for (int j = 0; j < 5; ++j)
+        if (overlap(workspace, nws, ins[j], inn[j])) return DFLASH_ERR_INVALID;
+    if (overlap(workspace, nws, out_tok, no) || overlap(workspace, nws, n_emit, nn)) return DFLASH_ERR_INVALID;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_verify_sample_hidden(h_t, W, draft, B, T, D, V, temperature, seed, request_id, pos0, out_tok,
+                                       n_emit, workspace, (hipStream_t)stream);
 }
 
 static int sample_common(const float* logits, const int32_t* draft, const int32_t* q_idx, const double* q_prob,

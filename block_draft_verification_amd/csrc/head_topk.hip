@@ -292,6 +292,70 @@ __device__ __forceinline__ void load_frag(u32x4& out, const uint16_t* row, int k
     }
 }
 
+// ------------------------------------------- softmax-statistics epilogue
+// For the sampling verifier fused into the target's LM head: instead of
+// top-16 lists, the head kernels write, per (row, 16-column vocabulary tile),
+// the tile's maximum logit m and s = sum over its columns of
+// exp((z - m) / tau), from the float32 accumulators (s in float32 through
+// v_exp_f32, so relative errors of ~1e-7 on top of the logits' own).
+struct TileStats {
+    float2* rec;      // [M][n16]
+    int64_t n16;      // tiles per row, ceil(V / 16)
+    float k2;         // (1 / tau) * log2(e)
+};
+
+__device__ __forceinline__ float dpp_f32(float x, int li, int which) {
+    const uint32_t u = __float_as_uint(x);
+    uint32_t r;
+    switch (which) {
+        case 1: r = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kDppX1, 0xF, 0xF, true); break;
+        case 2: r = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kDppX2, 0xF, 0xF, true); break;
+        case 8: r = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, kDppX8, 0xF, 0xF, true); break;
+        default: {  // lane ^ 4 inside the row
+            const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x104, 0xF, 0xF, true);
+            const uint32_t dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x114, 0xF, 0xF, true);
+            r = (li & 4) ? dn : up;
+        }
+    }
+    return __uint_as_float(r);
+}
+
+// acc[mt][nt][q] holds row grow0 + 16 mt + 4 (lane / 16) + q and column
+// col0 + nt * col_step + lane % 16 (tiles start at multiples of 16).
+template <int MW, int NT>
+__device__ __forceinline__ void stats_epilogue(const floatx4 (&acc)[MW][NT], const TileStats& st, int64_t grow0,
+                                               int64_t M, int64_t col0, int col_step, int nt_act, int64_t V,
+                                               int mw_act) {
+    const int lane = threadIdx.x & 63;
+    const int ln = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt) {
+        if (mt >= mw_act) continue;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt >= nt_act) continue;
+            const int64_t tc = col0 + (int64_t)nt * col_step;  // the tile's first column
+            const bool cok = tc + ln < V;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float z = acc[mt][nt][q];
+                float m = cok ? z : -INFINITY;
+                m = fmaxf(m, dpp_f32(m, ln, 1));
+                m = fmaxf(m, dpp_f32(m, ln, 2));
+                m = fmaxf(m, dpp_f32(m, ln, 4));
+                m = fmaxf(m, dpp_f32(m, ln, 8));
+                float e = cok ? __builtin_amdgcn_exp2f((z - m) * st.k2) : 0.0f;
+                e += dpp_f32(e, ln, 1);
+                e += dpp_f32(e, ln, 2);
+                e += dpp_f32(e, ln, 4);
+                e += dpp_f32(e, ln, 8);
+                const int64_t row = grow0 + mt * 16 + 4 * lg + q;
+                if (ln == 0 && row < M) st.rec[row * st.n16 + tc / 16] = make_float2(m, e);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------- skinny GEMM, LDS-staged W
 // The same wavefront-independent scheme, but W reaches the MFMAs through LDS
 // so that its HBM reads are row-contiguous: per chunk the wavefront's 16*NT
@@ -323,10 +387,10 @@ constexpr int kOffNone = 0x7FFFFFF0;      // a lane offset outside every resourc
 // Both operands are read row-contiguously into registers (two chunks in
 // flight), staged in the wavefront's LDS tile, and read back as MFMA
 // fragments.  h rows past M and W rows past V come back as zeros.
-template <int NTX, int KS>
+template <int NTX, int KS, bool STATS = false>
 __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const uint16_t* __restrict__ W,
                                               int64_t M, int D, int64_t V, int64_t row0, TopkRows tk,
-                                              unsigned char* __restrict__ wl) {
+                                              unsigned char* __restrict__ wl, const TileStats& st) {
     using C = Skinny2Cfg<NTX, KS>;
     constexpr int KC = C::KC;
     const int lane = threadIdx.x & 63;
@@ -416,7 +480,10 @@ __device__ __forceinline__ void skinny2_tiles(__amdgpu_buffer_rsrc_t hsrc, const
         stage(w0, h0);
         compute();
     }
-    topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, row0, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
+    if constexpr (STATS)
+        stats_epilogue<1, NTX>(acc, st, 0, M, row0, 16, NTX, V, 1);
+    else
+        topk_epilogue<1, NTX, false>(acc, tk, 0, 0, M, row0, 16, NTX, V, 1, (int)min<int64_t>(M, 16), 0, 4);
 }
 
 // WAVES wavefronts per workgroup (4 or 8).
@@ -429,12 +496,12 @@ struct SkinnyLds {
     static_assert(BYTES <= 160 * 1024, "LDS per workgroup");
 };
 
-template <int NT, int KS, int WAVES>
+template <int NT, int KS, int WAVES, bool STATS = false>
 __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t* __restrict__ h,
                                                                  const uint16_t* __restrict__ W, int64_t M,
                                                                  int D, int64_t V,
                                                                  float* __restrict__ part_val,
-                                                                 int* __restrict__ part_idx) {
+                                                                 int* __restrict__ part_idx, TileStats st) {
     using C = Skinny2Cfg<NT, KS>;
     using Lds = SkinnyLds<NT, KS, WAVES>;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -467,12 +534,21 @@ __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t
     // memory traffic) and the ids the epilogue admits.
     const int64_t nw = (int64_t)gridDim.x * WAVES;
     const int64_t gw = (int64_t)blockIdx.x * WAVES + wave;
-    const int64_t r_begin = gw * V / nw, r_end = (gw + 1) * V / nw;
     const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(h, M * D * 2);
+    if constexpr (STATS) {
+        // whole 16-row tiles (the statistics are kept per vocabulary tile)
+        const int64_t n_tiles = (V + 15) / 16;
+        const int64_t t_begin = gw * n_tiles / nw, t_end = (gw + 1) * n_tiles / nw;
+        int64_t t = t_begin;
+        for (; t + NT <= t_end; t += NT) skinny2_tiles<NT, KS, true>(hsrc, W, M, D, V, t * 16, tk, s_w, st);
+        for (; t < t_end; ++t) skinny2_tiles<1, KS, true>(hsrc, W, M, D, V, t * 16, tk, s_w, st);
+        return;
+    }
+    const int64_t r_begin = gw * V / nw, r_end = (gw + 1) * V / nw;
 
     int64_t row = r_begin;
-    for (; row + 16 * NT <= r_end; row += 16 * NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, r_end, row, tk, s_w);
-    for (; row < r_end; row += 16) skinny2_tiles<1, KS>(hsrc, W, M, D, r_end, row, tk, s_w);
+    for (; row + 16 * NT <= r_end; row += 16 * NT) skinny2_tiles<NT, KS>(hsrc, W, M, D, r_end, row, tk, s_w, st);
+    for (; row < r_end; row += 16) skinny2_tiles<1, KS>(hsrc, W, M, D, r_end, row, tk, s_w, st);
 
     // workgroup list per row: the wavefronts' lists merged in groups of four
     // (a 64-lane sort each), then the groups' leaders (a 32-lane sort)
@@ -557,11 +633,11 @@ __device__ __forceinline__ void with_slot(int k, F&& f) {
     }
 }
 
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false, bool STATS = false>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t M, int D,
                       int64_t V, int64_t n_tiles, int S, int n_mb, float* __restrict__ part_val,
-                      int* __restrict__ part_idx) {
+                      int* __restrict__ part_idx, TileStats st) {
     using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
     constexpr int KC = C::KC;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -719,9 +795,13 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
             compute(n_full);
             __syncthreads();
         }
-        topk_epilogue<MW, NT, true>(acc, tk, wm * 16 * MW, m0 + wm * 16 * MW, M, col0 + wn * 16, 16 * WN,
-                                    nt_act, V, mw_act, rows_blk, wave * 4, 8 * WN, t0 == t_begin);
+        if constexpr (STATS)
+            stats_epilogue<MW, NT>(acc, st, m0 + wm * 16 * MW, M, col0 + wn * 16, 16 * WN, nt_act, V, mw_act);
+        else
+            topk_epilogue<MW, NT, true>(acc, tk, wm * 16 * MW, m0 + wm * 16 * MW, M, col0 + wn * 16, 16 * WN,
+                                        nt_act, V, mw_act, rows_blk, wave * 4, 8 * WN, t0 == t_begin);
     }
+    if constexpr (STATS) return;
 
     for (int e = tid; e < rows_blk * kTopK; e += C::THREADS) {
         const int r = e / kTopK, k = e % kTopK;
@@ -1037,17 +1117,20 @@ struct HeadPlan {
 template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
 struct WideVariant {
     using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
+    template <bool STATS>
     static const void* fn() {
-        return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ>);
+        return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ, STATS>);
     }
     static void set_attr() {
-        (void)hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+        (void)hipFuncSetAttribute(fn<false>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+        (void)hipFuncSetAttribute(fn<true>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
     }
+    template <bool STATS = false>
     static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
-                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
+                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream, TileStats st = TileStats{}) {
         const int grid = (S + 7) / 8 * 8 * n_mb;
-        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ>), dim3(grid), dim3(Cfg::THREADS), Cfg::LDS, stream, h,
-                           W, M, D, V, n_tiles, S, n_mb, pv, pi);
+        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ, STATS>), dim3(grid), dim3(Cfg::THREADS),
+                           Cfg::LDS, stream, h, W, M, D, V, n_tiles, S, n_mb, pv, pi, st);
     }
 };
 
@@ -1120,11 +1203,13 @@ size_t head_workspace_bytes(int64_t M, int64_t V) {
     return b;
 }
 
-int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
-                     float* top_val, int32_t* top_idx, void* ws, hipStream_t stream) {
+static void set_head_attrs() {
     std::call_once(g_head_attr_once, []() {
         (void)hipFuncSetAttribute(
-            reinterpret_cast<const void*>(&head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves>),
+            reinterpret_cast<const void*>(&head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, false>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkinnyL::BYTES);
+        (void)hipFuncSetAttribute(
+            reinterpret_cast<const void*>(&head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, true>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkinnyL::BYTES);
         Wide128::set_attr();
         Wide224::set_attr();
@@ -1133,6 +1218,11 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLists * kTopK * 8);
     });
+}
+
+int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
+                     float* top_val, int32_t* top_idx, void* ws, hipStream_t stream) {
+    set_head_attrs();
     const HeadPlan p = head_plan(M, V);
     float* pv = reinterpret_cast<float*>(ws);
     int* pi = reinterpret_cast<int*>(pv + (size_t)M * p.S * kTopK);
@@ -1140,9 +1230,9 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
     int* cand_id = reinterpret_cast<int*>(cand_z + (size_t)M * kRescore);
     switch (p.variant) {
         case kSkinny:
-            hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves>), dim3(p.S),
+            hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, false>), dim3(p.S),
                                dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M,
-                               D, V, pv, pi);
+                               D, V, pv, pi, TileStats{});
             break;
         case kWide128:
             Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
@@ -1167,6 +1257,36 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
         if (st != DFLASH_OK) return st;
         hipLaunchKernelGGL(head_rank_kernel, dim3((unsigned)((M + kRankRows - 1) / kRankRows)), dim3(64 * kRankRows),
                            0, stream, M, V, cand_z, cand_id, top_val, top_idx);
+    }
+    return launch_status();
+}
+
+// The same GEMMs with the softmax-statistics epilogue: rec [M][ceil(V/16)]
+// float2 (tile maximum, tile sum of exp((z - m) * inv_tau)); no merge.
+size_t head_stats_bytes(int64_t M, int64_t V) { return (size_t)M * ((V + 15) / 16) * 8; }
+
+int launch_head_stats(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, double inv_tau,
+                      float2* rec, hipStream_t stream) {
+    set_head_attrs();
+    const HeadPlan p = head_plan(M, V);
+    const TileStats st{rec, (V + 15) / 16, (float)(inv_tau * 1.4426950408889634)};
+    switch (p.variant) {
+        case kSkinny:
+            hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, true>), dim3(p.S),
+                               dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M, D, V, nullptr, nullptr, st);
+            break;
+        case kWide128:
+            Wide128::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            break;
+        case kWide64:
+            Wide64::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            break;
+        case kWide128W:
+            Wide128W::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            break;
+        default:
+            Wide224::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            break;
     }
     return launch_status();
 }

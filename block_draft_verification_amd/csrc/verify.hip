@@ -515,6 +515,177 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
     }
 }
 
+// ============================== sampling fused into the target's LM head
+// The target head GEMM (launch_head_stats) leaves, per (row, 16-token tile),
+// the tile maximum m_i and s_i = sum of exp((z - m_i) / tau) over the tile,
+// from float32 logits.  One workgroup per request then decides the slots in
+// order as sample_decide_kernel does, with
+//   m = max_i m_i, Z = sum_i s_i exp((m_i - m) / tau)            (float64),
+//   e(d) from the draft's logit re-scored exactly (float64 dot product),
+// and on a rejection (or for the bonus) locates the tile holding the target
+// by a scan over the tile masses, re-scores that tile's 16 logits exactly and
+// inverts the CDF inside it (ascending ids, the draft weighted 0).  If
+// rounding leaves the target past the tile's exact mass, the tile's last
+// token of non-zero weight is taken.
+__device__ double exact_logit(const uint16_t* __restrict__ hr, const uint16_t* __restrict__ wr, int D, double* dscr) {
+    double acc = 0.0;
+    for (int k = threadIdx.x * 8; k < D; k += kVerifyThreads * 8) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(hr + k);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(wr + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = fma((double)bf16_to_f32(a[q] & 0xFFFFu), (double)bf16_to_f32(w[q] & 0xFFFFu), acc);
+            acc = fma((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(w[q] >> 16), acc);
+        }
+    }
+    return block_sum(acc, dscr);
+}
+
+__global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
+    const float2* __restrict__ rec, int64_t n16, const uint16_t* __restrict__ h_t, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ draft, int T, int D, int64_t V, double inv_tau, uint64_t seed,
+    const uint64_t* __restrict__ request_id, const int64_t* __restrict__ pos0, int32_t* __restrict__ out_tok,
+    int32_t* __restrict__ n_emit) {
+    __shared__ double dscr[4];
+    __shared__ float fscr[4];
+    __shared__ int iscr[4];
+    __shared__ double s_before;
+    __shared__ double s_u[2];
+    __shared__ double s_z[16];
+    __shared__ int s_tok;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int P = T - 1;
+    const uint64_t rid = request_id[b];
+    const int64_t p0 = pos0[b];
+    int32_t* o = out_tok + (int64_t)b * T;
+    int n = 0;
+    int emitted = -1;
+    for (int s = 1; s <= T && emitted < 0; ++s) {
+        const int t = (s <= P) ? s - 1 : T - 1;
+        const int64_t row = (int64_t)b * T + t;
+        const float2* rr = rec + row * n16;
+        const uint16_t* hr = h_t + row * D;
+        float mf = -INFINITY;
+        for (int64_t i = tid; i < n16; i += kVerifyThreads) mf = fmaxf(mf, rr[i].x);
+        mf = block_max(mf, fscr);
+        const double m = (double)mf;
+        double zp = 0.0;
+        for (int64_t i = tid; i < n16; i += kVerifyThreads) zp += (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+        const double Z = block_sum(zp, dscr);
+        if (tid == 0) {
+            const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
+            s_u[0] = (double)(r.w[0] >> 11) * 0x1p-53;
+            s_u[1] = (double)(r.w[1] >> 11) * 0x1p-53;
+        }
+        __syncthreads();
+        int skip = -1;
+        double ed = 0.0, target;
+        if (s <= P) {
+            const int d = draft[(int64_t)b * P + (s - 1)];
+            const bool d_ok = d >= 0 && (int64_t)d < V;
+            if (d_ok) ed = exp((exact_logit(hr, W + (int64_t)d * D, D, dscr) - m) * inv_tau);
+            if (s_u[0] * Z < ed) {
+                if (tid == 0) o[n] = d;
+                ++n;
+                __syncthreads();
+                continue;
+            }
+            skip = d_ok ? d : -1;
+            target = s_u[1] * (Z - ed);
+        } else {
+            target = s_u[1] * Z;
+        }
+        // the tile holding the target, from the tile masses (the draft's tile
+        // without the draft)
+        double before = 0.0;
+        int64_t hit = -1;
+        for (int64_t i0 = 0; i0 < n16 && hit < 0; i0 += kVerifyThreads) {
+            const int64_t i = i0 + tid;
+            double mass = 0.0;
+            if (i < n16) {
+                mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+                if (skip >= 0 && skip / 16 == i) mass = fmax(0.0, mass - ed);
+            }
+            double total;
+            const double excl = block_exclusive_scan(mass, dscr, total);
+            const int cand = (i < n16 && before + excl + mass > target) ? (int)(i - i0) : 0x7FFFFFFF;
+            const int first = block_min_int(cand, iscr);
+            if (first != 0x7FFFFFFF) {
+                if (tid == first) s_before = before + excl;
+                __syncthreads();
+                before = s_before;
+                hit = i0 + first;
+                __syncthreads();
+            } else {
+                before += total;
+            }
+        }
+        if (hit < 0) hit = n16 - 1;  // rounding left the target beyond the total: the last tile
+        // the hit tile's 16 logits, exactly: wavefront w takes tokens w, w + 4, ...
+        {
+            const int w = tid >> 6, l = tid & 63;
+            for (int k = w; k < 16; k += kVerifyThreads / 64) {
+                const int64_t v = hit * 16 + k;
+                double acc = 0.0;
+                if (v < V) {
+                    const uint16_t* wr = W + v * D;
+                    for (int kk = l * 8; kk < D; kk += 64 * 8) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(hr + kk);
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(wr + kk);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc = fma((double)bf16_to_f32(a[q] & 0xFFFFu), (double)bf16_to_f32(x[q] & 0xFFFFu), acc);
+                            acc = fma((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(x[q] >> 16), acc);
+                        }
+                    }
+                }
+                acc = wave_sum(acc);
+                if (l == 0) s_z[k] = acc;
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int tok = -1, last = -1;
+            double c = before;
+            for (int k = 0; k < 16; ++k) {
+                const int64_t v = hit * 16 + k;
+                if (v >= V || (int)v == skip) continue;
+                const double wv = exp((s_z[k] - m) * inv_tau);
+                if (wv > 0.0) last = (int)v;
+                c += wv;
+                if (tok < 0 && wv > 0.0 && c > target) tok = (int)v;
+            }
+            s_tok = tok >= 0 ? tok : (last >= 0 ? last : (int)(hit * 16));
+        }
+        __syncthreads();
+        emitted = s_tok;
+    }
+    if (tid == 0) {
+        o[n] = emitted;
+        for (int k = n + 1; k < T; ++k) o[k] = -1;
+        n_emit[b] = n + 1;
+    }
+}
+
+size_t head_stats_bytes(int64_t M, int64_t V);
+int launch_head_stats(const uint16_t*, const uint16_t*, int64_t, int, int64_t, double, float2*, hipStream_t);
+
+size_t sample_hidden_workspace_bytes(int B, int T, int64_t V) { return head_stats_bytes((int64_t)B * T, V); }
+
+int launch_verify_sample_hidden(const uint16_t* h_t, const uint16_t* W, const int32_t* draft, int B, int T, int D,
+                                int64_t V, float temperature, uint64_t seed, const uint64_t* request_id,
+                                const int64_t* pos0, int32_t* out_tok, int32_t* n_emit, void* ws,
+                                hipStream_t stream) {
+    const double inv_tau = 1.0 / (double)temperature;
+    float2* rec = reinterpret_cast<float2*>(ws);
+    int st = launch_head_stats(h_t, W, (int64_t)B * T, D, V, inv_tau, rec, stream);
+    if (st != DFLASH_OK) return st;
+    hipLaunchKernelGGL(sample_hidden_decide_kernel, dim3(B), dim3(kVerifyThreads), 0, stream, rec, (V + 15) / 16,
+                       h_t, W, draft, T, D, V, inv_tau, seed, request_id, pos0, out_tok, n_emit);
+    return launch_status();
+}
+
 // ================================================ top-k / top-p sampling
 // Source: latenode.com "DFlash 2: un drafter de 3.43x...", FAQ (the published
 // figures sample at temperature 1.0, top-p 0.95, top-k 20).  The target row is

@@ -20,6 +20,9 @@
  *                                general (sparse) proposal
  *   dflash_verify_greedy_fused   greedy verification from target hidden states,
  *                                the argmax taken in the LM-head GEMM epilogue
+ *   dflash_verify_sample_fused   rejection sampling from target hidden states,
+ *                                the softmax statistics taken in the LM-head
+ *                                GEMM epilogue
  *   dflash_verify_sample_topkp   rejection sampling against a top-k / top-p
  *                                filtered target
  *
@@ -238,6 +241,29 @@ int dflash_verify_greedy(const float* logits, const int32_t* draft, int32_t B,
 int dflash_verify_greedy_fused(const uint16_t* h_t, const uint16_t* W,
                                const int32_t* draft, int32_t B, int32_t T, int32_t D,
                                int64_t V, int32_t* out_tok, int32_t* n_emit,
+                               void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Rejection-sampling verification fused into the target LM head: as
+ * dflash_verify_sample on the logits z = h_t W^T, which are never written.
+ * The head GEMM's epilogue keeps, per (row, 16-token tile), the tile maximum
+ * and the tile sum of exp((z - m) / tau) from its float32 logits; the draft's
+ * logit and the 16 logits of the tile an inverse CDF lands in are re-scored
+ * exactly.  The decisions are those of dflash_verify_sample on the exact
+ * logits except where a uniform falls within the float32 error (~1e-6 of the
+ * row's mass) of a decision boundary.  If rounding leaves the inverse-CDF
+ * target past the landing tile's exact mass, that tile's last token of
+ * non-zero weight is emitted.
+ *   h_t, W as for dflash_verify_greedy_fused; the other arguments as for
+ *   dflash_verify_sample.
+ * Requires as dflash_verify_greedy_fused plus temperature finite and > 0.
+ * Workspace: B*T*ceil(V/16)*8 bytes.
+ */
+int dflash_verify_sample_fused(const uint16_t* h_t, const uint16_t* W,
+                               const int32_t* draft, int32_t B, int32_t T, int32_t D,
+                               int64_t V, float temperature, uint64_t seed,
+                               const uint64_t* request_id, const int64_t* pos0,
+                               int32_t* out_tok, int32_t* n_emit,
                                void* workspace, size_t* workspace_bytes, void* stream);
 
 /*

@@ -218,3 +218,16 @@ def test_greedy_fused_validation():
     assert call(h=None) == INVALID
     assert call(h=ctypes.c_void_p((1 << 40) + 8)) == INVALID         # h_t not 16-byte aligned
     assert call(out=P8[2]) == INVALID                                # out_tok overlaps the drafts
+
+
+@needs_lib
+def test_sample_fused_validation():
+    f = dfl.lib().dflash_verify_sample_fused
+    n = ctypes.c_size_t(0)
+    P8 = [ctypes.c_void_p((i + 1) << 40) for i in range(8)]
+    def call(B=8, T=8, D=5120, V=151936, tau=1.0, rid=P8[5], out=P8[3]):
+        return f(P8[0], P8[1], P8[2], B, T, D, V, tau, 0, rid, P8[6], out, P8[4], None, ctypes.byref(n), None)
+    assert call() == OK and n.value == 8 * 8 * 9496 * 8
+    assert call(tau=0.0) == INVALID and call(tau=float("nan")) == INVALID and call(rid=None) == INVALID
+    assert call(T=17) == INVALID and call(V=8) == INVALID and call(D=12) == INVALID
+    assert call(out=P8[2]) == INVALID

@@ -46,3 +46,31 @@ def test_matches_oracle(dfl, dev, B, T, D, V, grid):
     o0, n0 = verify_greedy_hidden(h, W, d)
     assert np.array_equal(n.cpu().numpy(), n0)
     assert np.array_equal(out.cpu().numpy(), o0)
+
+
+@pytest.mark.parametrize("B,T,D,V,tau,boost", [(8, 8, 256, 4096, 1.0, 6.0), (8, 8, 5120, 151936, 1.0, 8.0),
+                                               (3, 16, 512, 3001, 0.7, 5.0), (8, 8, 5120, 151936, 1.0, 0.0),
+                                               (16, 8, 1024, 20000, 1.3, 7.0)])
+def test_sample_fused_matches_oracle(dfl, dev, B, T, D, V, tau, boost):
+    """Exact agreement with the sampler on exact logits, except for requests
+    whose decisions lie within the float32 error of a boundary (margin 1e-5)."""
+    from oracle.verify import verify_sample_hidden
+    rng = np.random.default_rng(B + T + D + V)
+    W = (0.02 * rng.standard_normal((V, D))).astype(np.float32)
+    h = rng.standard_normal((B * T, D)).astype(np.float32)
+    d = rng.integers(0, V, (B, T - 1))
+    if boost > 0:  # target rows lean toward the drafts: acceptances
+        rows = (np.arange(B)[:, None] * T + np.arange(T - 1)[None]).ravel()
+        wd = W[d.ravel()]
+        h[rows] += (boost * wd / (wd ** 2).sum(1, keepdims=True)).astype(np.float32)
+    hb, Wb = bf16(h), bf16(W)
+    rid = np.arange(B, dtype=np.int64) * 11 + 3
+    pos0 = np.full(B, 512, np.int64)
+    out, n = dfl.verify_sample_fused(hb.to(dev), Wb.to(dev), torch.from_numpy(d.astype(np.int32)).to(dev), tau, 6,
+                                     torch.from_numpy(rid).to(dev), torch.from_numpy(pos0).to(dev))
+    torch.cuda.synchronize()
+    o0, n0, margin = verify_sample_hidden(hb, Wb, d, tau, 6, rid, pos0, return_margins=True)
+    out, n = out.cpu().numpy(), n.cpu().numpy()
+    same = (n == n0) & np.all(out == o0, axis=1)
+    assert np.all(same | (margin < 1e-5)), (np.nonzero(~same), margin[~same])
+    assert same.mean() >= 0.75
