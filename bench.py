@@ -62,8 +62,8 @@ def parse():
                     help="sampled requests draw their path from the lattice's chain distribution and are "
                          "verified against the proposals that drew it")
     ap.add_argument("--fused-target-head", action="store_true",
-                    help="greedy requests are verified from the target's hidden states through the shared LM "
-                         "head (argmax in the GEMM epilogue, no target logits)")
+                    help="requests are verified from the target's hidden states through the shared LM head "
+                         "(argmax or softmax statistics in the GEMM epilogue, no target logits)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -118,7 +118,10 @@ class CycleRunner:
         else:
             self.ws_g = torch.empty(dfl.workspace_bytes("verify_greedy", max(g, 1), T, cfg.V), dtype=u8,
                                     device=dev)
-        if cfg.top_k > 0:
+        if cfg.fused_target_head:
+            self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_fused", max(B - g, 1), T, cfg.D, cfg.V),
+                                    dtype=u8, device=dev)
+        elif cfg.top_k > 0:
             self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample_topkp", max(B - g, 1), T, cfg.V, cfg.top_k),
                                     dtype=u8, device=dev)
         else:
@@ -154,7 +157,11 @@ class CycleRunner:
         elif g > 0:
             ver.append(dfl.bind_verify_greedy(s["target_g"], self.tok[:g], self.out[:g], self.n[:g], self.ws_g))
         if g < B:
-            if cfg.sampled_path:
+            if cfg.fused_target_head:
+                ver.append(dfl.bind_verify_sample_fused(s["h_target_s"], self.W, self.tok[g:], cfg.temperature,
+                                                        cfg.seed, s["rid_s"], s["pos_s"], self.out[g:], self.n[g:],
+                                                        self.ws_s))
+            elif cfg.sampled_path:
                 ver.append(dfl.bind_verify_sample_q(s["target_s"], self.tok[g:], ti3[g:], self.q, cfg.temperature,
                                                     cfg.seed, s["rid_s"], s["pos_s"], self.out[g:], self.n[g:],
                                                     self.ws_s))
@@ -217,7 +224,8 @@ def make_sets(torch, cfg, inp, max_sets):
         "x": inp["x"], "taps": inp["taps"], "h": inp["h"], "anchor": inp["anchor"],
         "target_g": inp["target"][:g].contiguous() if g > 0 and not fused else None,
         "h_target_g": inp["h_target"][:g * cfg.T].contiguous() if g > 0 and fused else None,
-        "target_s": inp["target"][g:].contiguous() if g < B else None,
+        "target_s": inp["target"][g:].contiguous() if g < B and not fused else None,
+        "h_target_s": inp["h_target"][g * cfg.T:].contiguous() if g < B and fused else None,
         "rid_s": inp["request_id"][g:].contiguous(), "pos_s": inp["pos0"][g:].contiguous(),
     }
     per_set = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
@@ -273,10 +281,12 @@ def cycle_floor(cfg):
     head = max(head_bytes / hbm, 2.0 * cfg.M * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     sel = cfg.B * max(cfg.P - 1, 0) * 2 * 16 * cfg.r * 4 / hbm
     g = {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
-    if cfg.fused_target_head:  # the greedy requests' target head instead of their logits
-        mt = g * cfg.T
-        ver = max((cfg.V * cfg.D * 2 + mt * cfg.D * 2) / hbm, 2.0 * mt * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
-        ver += 4.0 * (cfg.B - g) * cfg.T * cfg.V / hbm
+    if cfg.fused_target_head:  # the target head over the block's rows instead of their logits
+        ver = 0.0
+        for mt in (g * cfg.T, (cfg.B - g) * cfg.T):  # one head call per verification kind
+            if mt > 0:
+                ver += max((cfg.V * cfg.D * 2 + mt * cfg.D * 2) / hbm,
+                           2.0 * mt * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     else:
         ver = 4.0 * cfg.B * cfg.T * cfg.V / hbm
     return {"conv": conv * 1e6, "head_topk": head * 1e6, "select_path": sel * 1e6, "verify": ver * 1e6}
@@ -358,8 +368,8 @@ def main():
     dev = torch.device("cuda:0")
     cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
                      sampled_path=args.sampled_path, fused_target_head=args.fused_target_head)
-    if cfg.fused_target_head and cfg.verify == "sample":
-        print("--fused-target-head needs greedy requests", file=sys.stderr)
+    if cfg.fused_target_head and (cfg.sampled_path or cfg.top_k > 0):
+        print("--fused-target-head verifies against the unfiltered target with the max-sum path", file=sys.stderr)
         sys.exit(2)
     if cfg.sampled_path and (cfg.top_k > 0 or cfg.verify == "greedy"):
         print("--sampled-path needs sampled verification without a top-k / top-p filter", file=sys.stderr)
@@ -443,8 +453,8 @@ def main():
                    **({"sample_filter": {"top_k": cfg.top_k, "top_p": cfg.top_p}} if cfg.top_k > 0 else {}),
                    **({"selector": "anchored on slot 0"} if cfg.anchored else {}),
                    **({"draft_path": "sampled from the lattice (proposal q verified)"} if cfg.sampled_path else {}),
-                   **({"greedy_verify": "from target hidden states through the shared LM head (argmax in the "
-                                        "GEMM epilogue, no target logits)"} if cfg.fused_target_head else {})},
+                   **({"target": "hidden states through the shared LM head (argmax or softmax statistics in "
+                                 "the GEMM epilogue, no target logits)"} if cfg.fused_target_head else {})},
         "roofline": head_roofline(cfg, head_us),
         "cycle_roofline": cycle_roofline(cfg, ms_graph),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),

@@ -566,12 +566,18 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
         const int64_t row = (int64_t)b * T + t;
         const float2* rr = rec + row * n16;
         const uint16_t* hr = h_t + row * D;
+        // each thread owns a contiguous run of tiles; loads unrolled so that
+        // several are in flight
+        const int64_t per = (n16 + kVerifyThreads - 1) / kVerifyThreads;
+        const int64_t i0 = min<int64_t>((int64_t)tid * per, n16), i1 = min<int64_t>(i0 + per, n16);
         float mf = -INFINITY;
-        for (int64_t i = tid; i < n16; i += kVerifyThreads) mf = fmaxf(mf, rr[i].x);
+#pragma unroll 8
+        for (int64_t i = i0; i < i1; ++i) mf = fmaxf(mf, rr[i].x);
         mf = block_max(mf, fscr);
         const double m = (double)mf;
-        double zp = 0.0;
-        for (int64_t i = tid; i < n16; i += kVerifyThreads) zp += (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+        double zp = 0.0;  // this run's mass
+#pragma unroll 8
+        for (int64_t i = i0; i < i1; ++i) zp += (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
         const double Z = block_sum(zp, dscr);
         if (tid == 0) {
             const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
@@ -597,52 +603,66 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
             target = s_u[1] * Z;
         }
         // the tile holding the target, from the tile masses (the draft's tile
-        // without the draft)
-        double before = 0.0;
-        int64_t hit = -1;
-        for (int64_t i0 = 0; i0 < n16 && hit < 0; i0 += kVerifyThreads) {
-            const int64_t i = i0 + tid;
-            double mass = 0.0;
-            if (i < n16) {
-                mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
-                if (skip >= 0 && skip / 16 == i) mass = fmax(0.0, mass - ed);
-            }
-            double total;
-            const double excl = block_exclusive_scan(mass, dscr, total);
-            const int cand = (i < n16 && before + excl + mass > target) ? (int)(i - i0) : 0x7FFFFFFF;
-            const int first = block_min_int(cand, iscr);
-            if (first != 0x7FFFFFFF) {
-                if (tid == first) s_before = before + excl;
-                __syncthreads();
-                before = s_before;
-                hit = i0 + first;
-                __syncthreads();
-            } else {
-                before += total;
-            }
+        // without the draft): each thread sums a contiguous run of tiles, one
+        // block scan finds the run holding the target, its thread walks it
+        auto tile_mass = [&](int64_t i) -> double {
+            double mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+            if (skip >= 0 && skip / 16 == i) mass = fmax(0.0, mass - ed);
+            return mass;
+        };
+        // the run's mass without the draft: its tile loses min(mass, e(d))
+        double run = zp;
+        if (skip >= 0 && skip / 16 >= i0 && skip / 16 < i1) {
+            const int64_t i = skip / 16;
+            const double mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+            run -= mass - fmax(0.0, mass - ed);
         }
-        if (hit < 0) hit = n16 - 1;  // rounding left the target beyond the total: the last tile
-        // the hit tile's 16 logits, exactly: wavefront w takes tokens w, w + 4, ...
+        double total;
+        const double excl = block_exclusive_scan(run, dscr, total);
+        const int owner = block_min_int(i0 < i1 && excl + run > target ? tid : 0x7FFFFFFF, iscr);
+        if (tid == (owner == 0x7FFFFFFF ? kVerifyThreads - 1 : owner)) {
+            // rounding can leave the target past the total: the last run then
+            int64_t hit_i = i1 > i0 ? i1 - 1 : n16 - 1;
+            double c = excl, before_i = excl;
+            for (int64_t i = i0; i < i1; ++i) {
+                const double w = tile_mass(i);
+                if (c + w > target) {
+                    hit_i = i;
+                    before_i = c;
+                    break;
+                }
+                c += w;
+                before_i = c - w;
+            }
+            s_before = before_i;
+            s_tok = (int)hit_i;
+        }
+        __syncthreads();
+        const double before = s_before;
+        const int64_t hit = s_tok;
+        __syncthreads();
+        // the hit tile's 16 logits, exactly: a group of 16 lanes per token
+        // (loads unrolled), summed across the group in a fixed order
         {
-            const int w = tid >> 6, l = tid & 63;
-            for (int k = w; k < 16; k += kVerifyThreads / 64) {
-                const int64_t v = hit * 16 + k;
-                double acc = 0.0;
-                if (v < V) {
-                    const uint16_t* wr = W + v * D;
-                    for (int kk = l * 8; kk < D; kk += 64 * 8) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(hr + kk);
-                        const u32x4 x = *reinterpret_cast<const u32x4*>(wr + kk);
+            const int k = tid >> 4, l = tid & 15;
+            const int64_t v = hit * 16 + k;
+            double acc = 0.0;
+            if (v < V) {
+                const uint16_t* wr = W + v * D;
+#pragma unroll 8
+                for (int kk = l * 8; kk < D; kk += 16 * 8) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(hr + kk);
+                    const u32x4 x = *reinterpret_cast<const u32x4*>(wr + kk);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            acc = fma((double)bf16_to_f32(a[q] & 0xFFFFu), (double)bf16_to_f32(x[q] & 0xFFFFu), acc);
-                            acc = fma((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(x[q] >> 16), acc);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        acc = fma((double)bf16_to_f32(a[q] & 0xFFFFu), (double)bf16_to_f32(x[q] & 0xFFFFu), acc);
+                        acc = fma((double)bf16_to_f32(a[q] >> 16), (double)bf16_to_f32(x[q] >> 16), acc);
                     }
                 }
-                acc = wave_sum(acc);
-                if (l == 0) s_z[k] = acc;
             }
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off, 16);
+            if (l == 0) s_z[k] = acc;
         }
         __syncthreads();
         if (tid == 0) {

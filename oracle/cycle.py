@@ -11,9 +11,9 @@ top-p filtered target (latenode.com, FAQ: the published figures sample with
 top-p 0.95 and top-k 20); with anchored=True the selector starts from each
 block's slot-0 token; with sampled_path=True (a reading beyond the pages) the
 sampled requests draw their path from the lattice's chain distribution and are
-verified against the proposals that drew it; with fused_target_head=True the
-greedy requests are verified from the target's hidden states through the
-shared LM head.
+verified against the proposals that drew it; with fused_target_head=True
+every request is verified from the target's hidden states through the shared
+LM head.
 """
 
 import numpy as np
@@ -21,7 +21,7 @@ import numpy as np
 from .conv import conv2tap
 from .head import head_topk
 from .selector import select_path, select_path_sampled
-from .verify import (verify_greedy, verify_greedy_hidden, verify_sample, verify_sample_q,
+from .verify import (verify_greedy, verify_greedy_hidden, verify_sample, verify_sample_hidden, verify_sample_q,
                      verify_sample_topkp)
 
 
@@ -55,7 +55,10 @@ def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=
         out[:g], n[:g] = verify_greedy_hidden(inp["h_target"][:g * T], inp["W"], tok[:g], chunk=head_chunk)
     elif g > 0:
         out[:g], n[:g] = verify_greedy(logits[:g], tok[:g])
-    if g < B and sampled_path:
+    if g < B and fused_target_head:
+        out[g:], n[g:] = verify_sample_hidden(inp["h_target"][g * T:], inp["W"], tok[g:], inp["temperature"],
+                                              inp["seed"], inp["request_id"][g:], inp["pos0"][g:], chunk=head_chunk)
+    elif g < B and sampled_path:
         out[g:], n[g:] = verify_sample_q(logits[g:], tok[g:], idx[g:], q, inp["temperature"], inp["seed"],
                                          inp["request_id"][g:], inp["pos0"][g:])
     elif g < B and top_k > 0:
