@@ -30,7 +30,7 @@ class Config:
     top_p: float = 1.0
     anchored: bool = False    # selector anchored on each block's slot-0 token
     sampled_path: bool = False  # sampled rows: the draft path is drawn (proposal q), verified against q
-    fused_target_head: bool = False  # greedy rows: verified from target hidden states (argmax in the LM head)
+    fused_target_head: bool = False  # verified from target hidden states through the LM head (no target logits)
     K: int = 16
     L: int = 5        # conv layer calls per cycle
     seed: int = 0
