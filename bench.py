@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--fused-target-head", action="store_true",
                     help="requests are verified from the target's hidden states through the shared LM head "
                          "(argmax or softmax statistics in the GEMM epilogue, no target logits)")
+    ap.add_argument("--fused-tap-proj", action="store_true",
+                    help="the conv call projects its taps from the hidden states itself "
+                         "(dflash_conv2tap_proj: the tap GEMM with the conv in its epilogue)")
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
@@ -85,7 +88,7 @@ def copy_probe(gib):
 class CycleRunner:
     """Pre-bound C-ABI calls for every rotating input set."""
 
-    def __init__(self, dfl, torch, cfg, sets, W, F_l, F_r):
+    def __init__(self, dfl, torch, cfg, sets, W, F_l, F_r, w_tap=None):
         self.dfl = dfl
         dev = W.device
         B, T, P, L = cfg.B, cfg.T, cfg.P, cfg.L
@@ -127,7 +130,7 @@ class CycleRunner:
         else:
             self.ws_s = torch.empty(dfl.workspace_bytes("verify_sample", max(B - g, 1), T, cfg.V), dtype=u8,
                                     device=dev)
-        self.F_l, self.F_r, self.W = F_l, F_r, W
+        self.F_l, self.F_r, self.W, self.w_tap = F_l, F_r, W, w_tap
         self.sets = sets
         self.calls = [self.bind_set(s) for s in sets]
 
@@ -135,7 +138,10 @@ class CycleRunner:
         """The cycle's C-ABI calls on input set s, bound to the current stream."""
         dfl, cfg, B, L, g = self.dfl, self.cfg, self.cfg.B, self.cfg.L, self.g
         tv3, ti3 = self.tv.view(B, cfg.P, 16), self.ti.view(B, cfg.P, 16)
-        conv = [dfl.bind_conv2tap(s["x"], s["taps"], self.y_all)]
+        if cfg.fused_tap_proj:
+            conv = [dfl.bind_conv2tap_proj(s["x"], self.w_tap, self.y_all)]
+        else:
+            conv = [dfl.bind_conv2tap(s["x"], s["taps"], self.y_all)]
         head = dfl.bind_head_topk(s["h"], self.W, self.tv, self.ti, self.ws_head)
         anchor = s["anchor"] if cfg.anchored else None
         if cfg.sampled_path and g < B:
@@ -221,7 +227,7 @@ def make_sets(torch, cfg, inp, max_sets):
     B, g = cfg.B, {"greedy": cfg.B, "sample": 0, "mixed": cfg.B // 2}[cfg.verify]
     fused = cfg.fused_target_head
     base = {
-        "x": inp["x"], "taps": inp["taps"], "h": inp["h"], "anchor": inp["anchor"],
+        "x": inp["x"], "taps": None if cfg.fused_tap_proj else inp["taps"], "h": inp["h"], "anchor": inp["anchor"],
         "target_g": inp["target"][:g].contiguous() if g > 0 and not fused else None,
         "h_target_g": inp["h_target"][:g * cfg.T].contiguous() if g > 0 and fused else None,
         "target_s": inp["target"][g:].contiguous() if g < B and not fused else None,
@@ -277,6 +283,9 @@ def cycle_floor(cfg):
     it gathers; verify: the target logits once."""
     hbm = HBM_PEAK_GBS * 1e9
     conv = 8.0 * cfg.L * cfg.B * cfg.T * cfg.D / hbm
+    if cfg.fused_tap_proj:  # x and y per token plus W_tap once, or the projection's MFMA time
+        conv = max((4.0 * cfg.L * cfg.B * cfg.T * cfg.D + 4.0 * cfg.D * cfg.D) / hbm,
+                   4.0 * cfg.L * cfg.B * cfg.T * cfg.D * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     head_bytes = cfg.V * cfg.D * 2 + cfg.M * cfg.D * 2 + cfg.M * 16 * 8
     head = max(head_bytes / hbm, 2.0 * cfg.M * cfg.V * cfg.D / (MFMA_BF16_PEAK_TFLOPS * 1e12))
     sel = cfg.B * max(cfg.P - 1, 0) * 2 * 16 * cfg.r * 4 / hbm
@@ -314,6 +323,47 @@ def stored_traffic(cfg):
     return entry.get("bytes_per_launch")
 
 
+def conv_proj_parity(torch, cfg, host, gpu_res, n_seq=8):
+    """The fused conv's outputs on n_seq sampled sequences of every layer
+    against the oracle's exact result: identical except on a bf16 rounding
+    boundary (the exact value within 1e-3 of its magnitude scale of the
+    midpoint of the two results), and such flips under 2 %."""
+    import numpy as np
+    from oracle.conv import conv2tap_proj
+    rng = np.random.default_rng(0)
+    flips = total = 0
+    for l in range(cfg.L):
+        seqs = rng.choice(cfg.B, min(n_seq, cfg.B), replace=False)
+        y_ref, y64, scale = conv2tap_proj(host["x"][l][seqs], host["w_tap"], return_exact=True)
+        g = gpu_res["y"][l][seqs].float().numpy().astype(np.float64)
+        r = y_ref.float().numpy().astype(np.float64)
+        diff = g != r
+        if np.any(diff & (np.abs(y64 - 0.5 * (g + r)) > 1e-3 * scale)):
+            return False
+        flips += int(diff.sum())
+        total += diff.size
+    return flips <= 0.02 * total
+
+
+def conv_proj_roofline(cfg, conv_us):
+    """The fused tap projection + conv against its roofline (HIP events around
+    the conv call): bf16 MFMA peak above the ridge, else HBM (W_tap once, x
+    read and y written)."""
+    rows = cfg.L * cfg.B * cfg.T
+    flops = 2.0 * rows * 2 * cfg.D * cfg.D
+    bytes_ = 4.0 * cfg.D * cfg.D + 4.0 * rows * cfg.D
+    t = conv_us * 1e-6
+    out = {"kernel": "conv_proj_kernel (dflash_conv2tap_proj)", "flops": int(flops),
+           "algorithmic_bytes": int(bytes_), "conv_us": round(conv_us, 2)}
+    if flops / bytes_ < MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = bytes_ / t / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), **out}
+    ach = flops / t / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), **out}
+
+
 def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
     """The oracle, as it stands, on the host's cores, on this run's inputs."""
     import numpy as np
@@ -323,19 +373,25 @@ def cpu_baseline(torch, cfg, inp, gpu_res, seconds):
     host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     t0 = time.perf_counter()
     ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
-              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head)
+              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head,
+              fused_tap_proj=cfg.fused_tap_proj)
     t1 = time.perf_counter() - t0
     n, total = 1, t1
     while total + t1 <= seconds and n < 200:
         t0 = time.perf_counter()
         run_cycle(host, cfg.B, cfg.T, verify=cfg.verify, top_k=cfg.top_k, top_p=cfg.top_p, anchored=cfg.anchored,
-              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head)
+              sampled_path=cfg.sampled_path, fused_target_head=cfg.fused_target_head,
+              fused_tap_proj=cfg.fused_tap_proj)
         total += time.perf_counter() - t0
         n += 1
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    if cfg.fused_tap_proj:
+        conv_ok = conv_proj_parity(torch, cfg, host, gpu_res)
+    else:
+        conv_ok = all(torch.equal(gpu_res["y"][l].view(torch.int16), ref["y"][l].view(torch.int16))
+                      for l in range(cfg.L))
     parity = {
-        "conv_bits": all(torch.equal(gpu_res["y"][l].view(torch.int16), ref["y"][l].view(torch.int16))
-                         for l in range(cfg.L)),
+        "conv_bits" if not cfg.fused_tap_proj else "conv_admissible": conv_ok,
         "top_idx": bool(np.array_equal(gpu_res["ti"], ref["top_idx"].reshape(-1, 16))),
         "path_tok": bool(np.array_equal(gpu_res["tok"], ref["path_tok"])),
         "out_tok": bool(np.array_equal(gpu_res["out"], ref["out_tok"])),
@@ -367,7 +423,8 @@ def main():
     dfl.lib()
     dev = torch.device("cuda:0")
     cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
-                     sampled_path=args.sampled_path, fused_target_head=args.fused_target_head)
+                     sampled_path=args.sampled_path, fused_target_head=args.fused_target_head,
+                     fused_tap_proj=args.fused_tap_proj)
     if cfg.fused_target_head and (cfg.sampled_path or cfg.top_k > 0):
         print("--fused-target-head verifies against the unfiltered target with the max-sum path", file=sys.stderr)
         sys.exit(2)
@@ -378,7 +435,7 @@ def main():
     inp = make_cycle_inputs(cfg, device=dev)
     sets, per_set = make_sets(torch, cfg, inp, args.max_sets)
     log(f"[bench] {len(sets)} rotating input sets of {per_set / 1e6:.1f} MB")
-    runner = CycleRunner(dfl, torch, cfg, sets, inp["W"], inp["F_l"], inp["F_r"])
+    runner = CycleRunner(dfl, torch, cfg, sets, inp["W"], inp["F_l"], inp["F_r"], inp["w_tap"])
 
     # warmup (untimed)
     for i in range(args.warmup):
@@ -454,9 +511,12 @@ def main():
                    **({"selector": "anchored on slot 0"} if cfg.anchored else {}),
                    **({"draft_path": "sampled from the lattice (proposal q verified)"} if cfg.sampled_path else {}),
                    **({"target": "hidden states through the shared LM head (argmax or softmax statistics in "
-                                 "the GEMM epilogue, no target logits)"} if cfg.fused_target_head else {})},
+                                 "the GEMM epilogue, no target logits)"} if cfg.fused_target_head else {}),
+                   **({"conv_taps": "projected from x in the conv call (5120 -> 10240 GEMM, conv in its "
+                                    "epilogue, taps never written)"} if cfg.fused_tap_proj else {})},
         "roofline": head_roofline(cfg, head_us),
         "cycle_roofline": cycle_roofline(cfg, ms_graph),
+        **({"conv_roofline": conv_proj_roofline(cfg, float(stage[:, 0].mean()))} if cfg.fused_tap_proj else {}),
         "stages_us": {"conv": round(float(np.median(stage[:, 0])), 2),
                       "head_topk": round(float(np.median(stage[:, 1])), 2),
                       "select_path": round(float(np.median(stage[:, 2])), 2),

@@ -6,6 +6,7 @@ fallback: if the library is missing or a call fails, an exception is raised.
 
 Entry points (same names and semantics as include/dflash.h):
     conv2tap(x, taps)                         -> y
+    conv2tap_proj(x, w_tap)                   -> y   (taps projected in the call)
     head_topk(h, W, K=16)                     -> (top_val, top_idx)
     select_path(top_val, top_idx, F_l, F_r)   -> (path_rank, path_tok, path_score)
     verify_greedy(logits, draft)              -> (out_tok, n_emit)
@@ -30,6 +31,7 @@ _SIGNATURES = {
     "dflash_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "dflash_version": (ctypes.c_int, []),
     "dflash_conv2tap": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
+    "dflash_conv2tap_proj": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
     "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
     "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                           _p, _p, _p, _p, _psz, _p]),
@@ -124,6 +126,22 @@ def conv2tap(x, taps, out=None):
     _need(y, torch.bfloat16, "out")
     _check(lib().dflash_conv2tap(_ptr(x), _ptr(taps), _ptr(y), S, T, D, _stream(x.device)),
            "dflash_conv2tap")
+    return y
+
+
+def conv2tap_proj(x, w_tap, out=None):
+    """x bf16 [S][T][D], w_tap bf16 [2D][D] -> y bf16 [S][T][D]."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_tap, torch.bfloat16, "w_tap")
+    D = x.shape[-1]
+    T = x.shape[-2]
+    S = x.numel() // (T * D)
+    if tuple(w_tap.shape) != (2 * D, D):
+        raise DFlashError("w_tap must be [2*D][D]")
+    y = torch.empty_like(x) if out is None else out
+    _need(y, torch.bfloat16, "out")
+    _check(lib().dflash_conv2tap_proj(_ptr(x), _ptr(w_tap), _ptr(y), S, T, D, _stream(x.device)),
+           "dflash_conv2tap_proj")
     return y
 
 
@@ -388,6 +406,16 @@ def _bound(fn, args, what):
         if code != 0:
             raise DFlashError(f"{what}: {status_string(code)} ({code})")
     return call
+
+
+def bind_conv2tap_proj(x, w_tap, y):
+    _need(x, torch.bfloat16, "x")
+    _need(w_tap, torch.bfloat16, "w_tap")
+    _need(y, torch.bfloat16, "y")
+    D, T = x.shape[-1], x.shape[-2]
+    S = x.numel() // (T * D)
+    return _bound(lib().dflash_conv2tap_proj, (_ptr(x), _ptr(w_tap), _ptr(y), S, T, D, _stream(x.device)),
+                  "dflash_conv2tap_proj")
 
 
 def bind_conv2tap(x, taps, y):

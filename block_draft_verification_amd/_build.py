@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libdflash.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "conv2tap.hip", "head_topk.hip", "select_path.hip", "verify.hip"]
+SOURCES = ["api.cpp", "conv2tap.hip", "conv_proj.hip", "head_topk.hip", "select_path.hip", "verify.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

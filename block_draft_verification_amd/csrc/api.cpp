@@ -12,6 +12,7 @@
 
 namespace dflash {
 int launch_conv2tap(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int, hipStream_t);
+int launch_conv2tap_proj(const uint16_t*, const uint16_t*, uint16_t*, int64_t, int, int, hipStream_t);
 int launch_head_topk(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*, void*,
                      hipStream_t);
 size_t head_workspace_bytes(int64_t M, int64_t V);
@@ -109,6 +110,19 @@ int dflash_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y, int64_
     int st = check_device();
     if (st != DFLASH_OK) return st;
     return launch_conv2tap(x, taps, y, n_seq, T, D, (hipStream_t)stream);
+}
+
+int dflash_conv2tap_proj(const uint16_t* x, const uint16_t* w_tap, uint16_t* y, int64_t n_seq, int32_t T,
+                         int32_t D, void* stream) {
+    if (!x || !w_tap || !y) return DFLASH_ERR_INVALID;
+    if (n_seq < 1 || T < 1 || T > 16 || D < 64 || D > 65536 || D % 64 != 0) return DFLASH_ERR_INVALID;
+    if (n_seq > ((int64_t)1 << 40) / ((int64_t)T * D)) return DFLASH_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(w_tap) || !aligned16(y)) return DFLASH_ERR_INVALID;
+    const size_t nx = (size_t)n_seq * T * D * 2, nw = (size_t)2 * D * D * 2;
+    if (overlap(y, nx, x, nx) || overlap(y, nx, w_tap, nw)) return DFLASH_ERR_INVALID;
+    int st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_conv2tap_proj(x, w_tap, y, n_seq, T, D, (hipStream_t)stream);
 }
 
 int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,

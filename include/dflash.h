@@ -10,8 +10,10 @@
  *   dflash_verify_greedy  greedy longest-prefix acceptance
  *   dflash_verify_sample  rejection-sampling acceptance (Philox4x64-10 draws)
  *
- * and two variants:
+ * and variants:
  *
+ *   dflash_conv2tap_proj         the conv with its taps projected from the
+ *                                hidden states inside the call (never written)
  *   dflash_select_path_anchored  the selector with the block's slot-0 token as
  *                                a fixed first column
  *   dflash_select_path_sampled   a path drawn from the lattice's chain
@@ -101,6 +103,26 @@ int dflash_version(void);
  */
 int dflash_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y,
                     int64_t n_seq, int32_t T, int32_t D, void* stream);
+
+/*
+ * The two-tap dynamic conv with its taps produced in the same call by the
+ * drafter's tap projection, so that the taps never reach memory.
+ * Source: as dflash_conv2tap; "dynamic" taps are read as a linear function of
+ * the token's own hidden state:
+ *     [a | b][s][t] = x[s][t] W_tap^T  (float32 accumulation of exact bf16
+ *                                       products; a = columns 0..D-1, b = D..2D-1)
+ *     y[s][t][c] = bf16_rne(fmaf(a, x[s][t][c], b * x[s][t-1][c])),
+ *     x[s][-1][c] = 0.
+ * The taps keep float32 precision (they are never rounded to bf16), so y
+ * differs from dflash_conv2tap on bf16-rounded taps; against the exact
+ * result it differs only by the rounding of a float32 sum.
+ *   x      bf16 [n_seq][T][D]   draft hidden states (one sequence = one block)
+ *   w_tap  bf16 [2*D][D]        tap projection (rows 0..D-1 give a, D..2D-1 b)
+ *   y      bf16 [n_seq][T][D]   output; must not overlap x or w_tap
+ * Requires n_seq >= 1, 1 <= T <= 16, 64 <= D <= 65536, D % 64 == 0.
+ */
+int dflash_conv2tap_proj(const uint16_t* x, const uint16_t* w_tap, uint16_t* y,
+                         int64_t n_seq, int32_t T, int32_t D, void* stream);
 
 /*
  * Draft LM head fused with top-K retention per row.

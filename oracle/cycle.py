@@ -13,12 +13,13 @@ block's slot-0 token; with sampled_path=True (a reading beyond the pages) the
 sampled requests draw their path from the lattice's chain distribution and are
 verified against the proposals that drew it; with fused_target_head=True
 every request is verified from the target's hidden states through the shared
-LM head.
+LM head; with fused_tap_proj=True the convs take their taps from the drafter's
+tap projection of x (inp["w_tap"]), unrounded, instead of the given bf16 taps.
 """
 
 import numpy as np
 
-from .conv import conv2tap
+from .conv import conv2tap, conv2tap_proj
 from .head import head_topk
 from .selector import select_path, select_path_sampled
 from .verify import (verify_greedy, verify_greedy_hidden, verify_sample, verify_sample_hidden, verify_sample_q,
@@ -26,9 +27,12 @@ from .verify import (verify_greedy, verify_greedy_hidden, verify_sample, verify_
 
 
 def run_cycle(inp, B, T, K=16, verify="greedy", head_chunk=8192, top_k=0, top_p=1.0, anchored=False,
-              sampled_path=False, fused_target_head=False):
+              sampled_path=False, fused_target_head=False, fused_tap_proj=False):
     L = inp["x"].shape[0]
-    ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
+    if fused_tap_proj:
+        ys = [conv2tap_proj(inp["x"][l], inp["w_tap"]) for l in range(L)]
+    else:
+        ys = [conv2tap(inp["x"][l], inp["taps"][l]) for l in range(L)]
     vals, idx, _ = head_topk(inp["h"], inp["W"], K=K, chunk=head_chunk)
     P = T - 1
     vals = vals.reshape(B, P, K)

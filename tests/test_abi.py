@@ -75,6 +75,23 @@ def test_conv_validation():
 
 
 @needs_lib
+def test_conv_proj_validation():
+    f = dfl.lib().dflash_conv2tap_proj
+    assert f(A[0], NULL, A[2], 1, 8, 64, NULL) == INVALID
+    assert f(A[0], A[1], A[2], 0, 8, 64, NULL) == INVALID          # n_seq
+    assert f(A[0], A[1], A[2], 1, 0, 64, NULL) == INVALID          # T < 1
+    assert f(A[0], A[1], A[2], 1, 17, 64, NULL) == INVALID         # T > 16
+    assert f(A[0], A[1], A[2], 1, 8, 32, NULL) == INVALID          # D < 64
+    assert f(A[0], A[1], A[2], 1, 8, 96, NULL) == INVALID          # D % 64
+    assert f(A[0], A[1], A[0], 1, 8, 64, NULL) == INVALID          # y == x
+    assert f(A[0], A[1], A[1], 1, 8, 64, NULL) == INVALID          # y == w_tap
+    assert f(A[0], A[1], ctypes.c_void_p((2 << 40) + 4096), 1, 8, 64, NULL) == INVALID  # y inside w_tap
+    assert f(A[0], ctypes.c_void_p((2 << 40) + 8), A[2], 1, 8, 64, NULL) == INVALID  # misaligned
+    if not torch.cuda.is_available():
+        assert f(A[0], A[1], A[2], 1, 8, 64, NULL) == DEVICE
+
+
+@needs_lib
 def test_head_validation_and_workspace():
     f = dfl.lib().dflash_head_topk
     st, need = ws_query(f, A[0], A[1], 7, 5120, 151936, 16, A[2], A[3])

@@ -76,3 +76,57 @@ def test_linear_in_taps_on_grid():
     y2 = conv2tap(x, bf16(t2)).float()
     y12 = conv2tap(x, bf16(t1 + t2)).float()
     assert torch.equal(y1 + y2, y12)
+
+
+# --- the conv on projected taps (oracle.conv.conv2tap_proj) ---
+
+def test_proj_diagonal_projection_closed_form():
+    """W_tap = [alpha I; beta I] gives a = alpha x, b = beta x, so
+    y[t] = alpha x[t]^2 + beta x[t] x[t-1] (small integers: exact)."""
+    from oracle.conv import conv2tap_proj
+    rng = np.random.default_rng(11)
+    S, T, D = 3, 6, 16
+    x = rng.integers(-6, 7, (S, T, D)).astype(np.float32)
+    alpha, beta = 2.0, -0.5
+    w = np.concatenate([alpha * np.eye(D), beta * np.eye(D)]).astype(np.float32)
+    y = conv2tap_proj(bf16(x), bf16(w)).float().numpy()
+    prev = np.concatenate([np.zeros((S, 1, D)), x[:, :-1]], axis=1)
+    assert np.array_equal(y, alpha * x * x + beta * x * prev)
+
+
+def test_proj_equals_conv_on_exact_taps_brute_force():
+    """Against pure-Python loops on a tiny case: taps t[s][t][j] = sum_k
+    x[s][t][k] W[j][k] (j < D gives a, j >= D gives b), then the direct conv.
+    Integer inputs keep every tap exactly representable in bf16, so the
+    result also equals the plain conv on those taps."""
+    from oracle.conv import conv2tap_proj
+    rng = np.random.default_rng(12)
+    S, T, D = 2, 4, 3
+    x = rng.integers(-3, 4, (S, T, D))
+    w = rng.integers(-2, 3, (2 * D, D))
+    taps = np.zeros((S, T, 2 * D))
+    for s in range(S):
+        for t in range(T):
+            for j in range(2 * D):
+                taps[s, t, j] = sum(int(x[s, t, k]) * int(w[j, k]) for k in range(D))
+    ref = np.zeros((S, T, D))
+    for s in range(S):
+        for t in range(T):
+            for c in range(D):
+                prev = x[s, t - 1, c] if t > 0 else 0
+                ref[s, t, c] = taps[s, t, c] * x[s, t, c] + taps[s, t, D + c] * prev
+    y = conv2tap_proj(bf16(x), bf16(w))
+    assert np.array_equal(y.float().numpy(), ref)
+    assert torch.equal(y.view(torch.int16), conv2tap(bf16(x), bf16(taps)).view(torch.int16))
+
+
+def test_proj_exact_value_and_scale():
+    """The unrounded value rounds to the returned bf16, and the scale bounds
+    the value (|y| <= |a x| + |b x_prev| <= scale)."""
+    from oracle.conv import conv2tap_proj
+    x = rand_bf16((2, 8, 32), 13)
+    w = (0.05 * torch.randn(64, 32, generator=torch.Generator().manual_seed(14))).to(torch.bfloat16)
+    y, y64, scale = conv2tap_proj(x, w, return_exact=True)
+    assert torch.equal(y.view(torch.int16), bf16(y64.astype(np.float32)).view(torch.int16))
+    assert np.all(np.abs(y64) <= scale)
+    assert np.all(np.isfinite(y64))

@@ -31,6 +31,7 @@ class Config:
     anchored: bool = False    # selector anchored on each block's slot-0 token
     sampled_path: bool = False  # sampled rows: the draft path is drawn (proposal q), verified against q
     fused_target_head: bool = False  # verified from target hidden states through the LM head (no target logits)
+    fused_tap_proj: bool = False  # conv taps projected from x inside the conv call (never written)
     K: int = 16
     L: int = 5        # conv layer calls per cycle
     seed: int = 0

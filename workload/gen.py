@@ -157,7 +157,7 @@ def make_cycle_inputs(cfg, device="cpu"):
     pos0 = 4096 + 64 * torch.arange(B, dtype=torch.int64, device=dev)
     h_target = torch.cat([ht_rows, ht_bonus.view(B, 1, D)], dim=1).reshape(B * T, D).to(torch.bfloat16)
     return {
-        "x": x, "taps": taps, "h": h, "W": W, "F_l": F_l, "F_r": F_r,
+        "x": x, "taps": taps, "w_tap": w_tap, "h": h, "W": W, "F_l": F_l, "F_r": F_r,
         "target": target, "h_target": h_target, "request_id": request_id, "pos0": pos0, "anchor": anchor,
         "planted": planted, "temperature": float(cfg.temperature),
         "seed": int(cfg.seed),
