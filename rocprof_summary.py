@@ -25,7 +25,7 @@ TRAFFIC = os.path.join(ROOT, "profiles", "head_topk_traffic.json")
 
 
 def short(name):
-    name = name.split("(")[0]
+    name = name.replace("(anonymous namespace)::", "").split("(")[0]
     return name[5:] if name.startswith("void ") else name
 
 
