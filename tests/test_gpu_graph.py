@@ -15,19 +15,31 @@ from workload import get_config, make_cycle_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _cycle(dfl, g, cfg, bufs, bound):
-    B, P = cfg.B, cfg.P
+def _cycle(dfl, g, cfg, bufs, bound, fused=False):
+    """fused: the conv projects its own taps, and verification runs from the
+    target's hidden states through the LM head."""
+    B, P, T = cfg.B, cfg.P, cfg.T
     calls = []
     for l in range(cfg.L):
-        calls.append(bound.bind_conv2tap(g["x"][l], g["taps"][l], bufs["y"][l]))
+        if fused:
+            calls.append(bound.bind_conv2tap_proj(g["x"][l], g["w_tap"], bufs["y"][l]))
+        else:
+            calls.append(bound.bind_conv2tap(g["x"][l], g["taps"][l], bufs["y"][l]))
     calls.append(bound.bind_head_topk(g["h"], g["W"], bufs["tv"], bufs["ti"], bufs["ws_h"]))
     calls.append(bound.bind_select_path(bufs["tv"].view(B, P, 16), bufs["ti"].view(B, P, 16), g["F_l"], g["F_r"],
                                         bufs["rank"], bufs["tok"], bufs["score"], bufs["ws_s"]))
     h = B // 2
-    calls.append(bound.bind_verify_greedy(g["target"][:h], bufs["tok"][:h], bufs["out"][:h], bufs["n"][:h],
-                                          bufs["ws_g"]))
-    calls.append(bound.bind_verify_sample(g["target"][h:], bufs["tok"][h:], 1.0, 7, g["request_id"][h:],
-                                          g["pos0"][h:], bufs["out"][h:], bufs["n"][h:], bufs["ws_v"]))
+    if fused:
+        calls.append(bound.bind_verify_greedy_fused(g["h_target"][:h * T], g["W"], bufs["tok"][:h], bufs["out"][:h],
+                                                    bufs["n"][:h], bufs["ws_g"]))
+        calls.append(bound.bind_verify_sample_fused(g["h_target"][h * T:], g["W"], bufs["tok"][h:], 1.0, 7,
+                                                    g["request_id"][h:], g["pos0"][h:], bufs["out"][h:],
+                                                    bufs["n"][h:], bufs["ws_v"]))
+    else:
+        calls.append(bound.bind_verify_greedy(g["target"][:h], bufs["tok"][:h], bufs["out"][:h], bufs["n"][:h],
+                                              bufs["ws_g"]))
+        calls.append(bound.bind_verify_sample(g["target"][h:], bufs["tok"][h:], 1.0, 7, g["request_id"][h:],
+                                              g["pos0"][h:], bufs["out"][h:], bufs["n"][h:], bufs["ws_v"]))
     for c in calls:
         c()
 
@@ -47,9 +59,10 @@ def _same(a, b):
     return True
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name, overrides", [("c1_tiny", {"B": 4, "name": "c1_graph_b4"}),
                                               ("c1_tiny", {"B": 8, "D": 1024, "V": 20000, "name": "c1_graph_b8"})])
-def test_graph_replays_equal_eager(dfl, dev, name, overrides):
+def test_graph_replays_equal_eager(dfl, dev, name, overrides, fused):
     cfg = get_config(name, **overrides)
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_cycle_inputs(cfg).items()}
     B, T, P, M = cfg.B, cfg.T, cfg.P, cfg.M
@@ -65,16 +78,18 @@ def test_graph_replays_equal_eager(dfl, dev, name, overrides):
         "n": torch.empty((B,), dtype=torch.int32, device=dev),
         "ws_h": torch.empty(dfl.workspace_bytes("head_topk", M, cfg.D, cfg.V), dtype=u8, device=dev),
         "ws_s": torch.empty(dfl.workspace_bytes("select_path", B, P), dtype=u8, device=dev),
-        "ws_g": torch.empty(dfl.workspace_bytes("verify_greedy", B // 2, T, cfg.V), dtype=u8, device=dev),
-        "ws_v": torch.empty(dfl.workspace_bytes("verify_sample", B - B // 2, T, cfg.V), dtype=u8, device=dev),
+        "ws_g": torch.empty(dfl.workspace_bytes("verify_greedy_fused", B // 2, T, cfg.D, cfg.V) if fused else
+                            dfl.workspace_bytes("verify_greedy", B // 2, T, cfg.V), dtype=u8, device=dev),
+        "ws_v": torch.empty(dfl.workspace_bytes("verify_sample_fused", B - B // 2, T, cfg.D, cfg.V) if fused else
+                            dfl.workspace_bytes("verify_sample", B - B // 2, T, cfg.V), dtype=u8, device=dev),
     }
-    _cycle(dfl, g, cfg, bufs, dfl)
+    _cycle(dfl, g, cfg, bufs, dfl, fused)
     torch.cuda.synchronize()
     eager = _snapshot(bufs)
 
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _cycle(dfl, g, cfg, bufs, dfl)
+        _cycle(dfl, g, cfg, bufs, dfl, fused)
     for rep in range(3):
         for v in bufs.values():  # scribble over the outputs between replays
             for t in (v if isinstance(v, list) else [v]):
@@ -85,6 +100,6 @@ def test_graph_replays_equal_eager(dfl, dev, name, overrides):
         graph.replay()
         torch.cuda.synchronize()
         assert _same(_snapshot(bufs), eager), f"replay {rep} differs from the eager cycle"
-        _cycle(dfl, g, cfg, bufs, dfl)  # eager work between replays
+        _cycle(dfl, g, cfg, bufs, dfl, fused)  # eager work between replays
         torch.cuda.synchronize()
         assert _same(_snapshot(bufs), eager)
