@@ -252,3 +252,41 @@ def test_fused_target_head_cycle(dfl, dev):
                                                 inp["pos0"][g:], return_margins=True)
             same = (n[g:] == ref["n_emit"][g:]) & np.all(out[g:] == ref["out_tok"][g:], axis=1)
             assert np.all(same | (margin < 1e-5)), (name, np.nonzero(~same), margin[~same])
+
+
+def _requests(inp, cfg, idx):
+    """The inputs of requests idx (in that order) as a batch of their own."""
+    idx_t = torch.as_tensor(idx, device=inp["h"].device)
+    P = cfg.P
+    rows = (idx_t[:, None] * P + torch.arange(P, device=idx_t.device)[None]).reshape(-1)
+    out = dict(inp)
+    out["x"] = inp["x"][:, idx_t].contiguous()
+    out["taps"] = inp["taps"][:, idx_t].contiguous()
+    out["h"] = inp["h"][rows].contiguous()
+    for k in ("target", "request_id", "pos0", "anchor"):
+        out[k] = inp[k][idx_t].contiguous()
+    return out
+
+
+@pytest.mark.parametrize("name", ["c3_b8", "c2_b1"])
+def test_cycle_batch_composition_invariance(dfl, dev, name):
+    """A request's whole cycle (conv, top-16 lists, path, emitted tokens) is
+    bit-identical whether it runs alone, in another batch position, or next
+    to other requests; the draws are keyed by (seed, request id, position),
+    and a lone request goes through the other LM-head kernel (M <= 16)."""
+    import dataclasses
+    cfg = get_config(name, name=name + "_compose", B=8, D=512, V=8000)
+    d = to_dev(make_cycle_inputs(cfg), dev)
+    full = gpu_cycle(dfl, d, cfg)
+    rng = np.random.default_rng(3)
+    for idx in ([5], [0], list(rng.permutation(8)), [6, 2, 7]):
+        sub_cfg = dataclasses.replace(cfg, B=len(idx))
+        sub = gpu_cycle(dfl, _requests(d, cfg, idx), sub_cfg)
+        P = cfg.P
+        for j, r in enumerate(idx):
+            for l in range(cfg.L):
+                assert torch.equal(sub["y"][l][j].view(torch.int16), full["y"][l][r].view(torch.int16))
+            assert torch.equal(sub["top_idx"][j], full["top_idx"][r]), (idx, r)
+            assert torch.equal(sub["path_tok"][j], full["path_tok"][r]), (idx, r)
+            assert torch.equal(sub["out_tok"][j], full["out_tok"][r]), (idx, r)
+            assert torch.equal(sub["n_emit"][j], full["n_emit"][r]), (idx, r)
