@@ -12,8 +12,8 @@
 // full even for a single sequence.  A thread reads its row's x and taps and
 // the previous row's x (the same bytes the neighbouring thread reads as its
 // own x, so that read hits the cache).  Calls of 2^20 threads or more give each
-// thread four consecutive rows instead, keeping x[t-1] in registers inside the
-// group.  Algorithmic HBM traffic per element: x 2 B + taps 4 B + y 2 B.
+// thread four consecutive rows instead (2^19 or more: two), keeping x[t-1] in
+// registers inside the group.  Algorithmic HBM traffic per element: x 2 B + taps 4 B + y 2 B.
 //
 // Arithmetic: bf16 x bf16 products are exact in float32, so fmaf(a, x, b*xp)
 // rounds the exact sum once; the result is rounded to bf16 nearest-even.
@@ -90,13 +90,17 @@ int launch_conv2tap(const uint16_t* x, const uint16_t* taps, uint16_t* y, int64_
     const u32x4* xv = reinterpret_cast<const u32x4*>(x);
     const u32x4* tv = reinterpret_cast<const u32x4*>(taps);
     u32x4* yv = reinterpret_cast<u32x4*>(y);
-    // large calls (the block-16, batch-32, five-layer shape: 105 MB, 20.0 ->
-    // 18.7 us measured): four rows per thread, a quarter of the workgroups and
-    // of the x[t-1] re-reads; smaller ones keep one row per thread, which
-    // measured as fast or faster (block 8, batch 32: 11.1 against 11.6 us)
+    // large calls (the block-16, batch-32, five-layer shape: 105 MB, 20.2 ->
+    // 17.4 us measured): four rows per thread, a quarter of the workgroups and
+    // of the x[t-1] re-reads; mid-sized ones (block 8, batch 32, five layers:
+    // 52 MB) two rows per thread (9.9 -> 8.5 us; four rows: 9.7 us); small
+    // ones one row per thread, the most threads for the memory queues
     if (n_rows * D8 >= (int64_t)CONV_R4_MIN) {
         const int64_t grid = ((n_rows + 3) / 4 * D8 + block - 1) / block;
         hipLaunchKernelGGL(conv2tap_kernel<4>, dim3((unsigned)grid), dim3(block), 0, stream, xv, tv, yv, n_rows, T, D8);
+    } else if (n_rows * D8 >= (int64_t)CONV_R4_MIN / 2) {
+        const int64_t grid = ((n_rows + 1) / 2 * D8 + block - 1) / block;
+        hipLaunchKernelGGL(conv2tap_kernel<2>, dim3((unsigned)grid), dim3(block), 0, stream, xv, tv, yv, n_rows, T, D8);
     } else {
         const int64_t grid = (n_rows * D8 + block - 1) / block;
         hipLaunchKernelGGL(conv2tap_kernel<1>, dim3((unsigned)grid), dim3(block), 0, stream, xv, tv, yv, n_rows, T, D8);

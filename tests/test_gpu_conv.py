@@ -61,3 +61,16 @@ def test_conv_large_calls_four_rows_per_thread(dfl, dev, S, T, D):
     taps = rand_bf16((S, T, 2 * D), S + T + 1, sd=1.4)
     y = dfl.conv2tap(x.to(dev), taps.to(dev)).cpu()
     assert torch.equal(y.view(torch.int16), oracle_conv(x, taps).view(torch.int16))
+
+
+@pytest.mark.parametrize("S,T,D", [(160, 8, 5120), (101, 7, 6144), (1025, 1, 4096), (93, 15, 4104)])
+def test_conv_mid_calls_two_rows_per_thread(dfl, dev, S, T, D):
+    """Calls of 2^19 to 2^20 threads (the five-layer block-8 batch-32 shape
+    among them) take two token rows per thread; pairs straddle sequence
+    starts when T is odd, and the last pair is ragged when S*T is odd."""
+    n = S * T * D // 8
+    assert (1 << 19) <= n < (1 << 20)
+    x = rand_bf16((S, T, D), S + T + 7)
+    taps = rand_bf16((S, T, 2 * D), S + T + 8, sd=1.4)
+    y = dfl.conv2tap(x.to(dev), taps.to(dev)).cpu()
+    assert torch.equal(y.view(torch.int16), oracle_conv(x, taps).view(torch.int16))
