@@ -33,6 +33,7 @@ _SIGNATURES = {
     "dflash_conv2tap": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
     "dflash_conv2tap_proj": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
     "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
+    "dflash_head_topk_noalloc": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p]),
     "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                           _p, _p, _p, _p, _psz, _p]),
     "dflash_select_path_anchored": (ctypes.c_int, [_p, _p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
@@ -163,6 +164,25 @@ def head_topk(h, W, K=16, workspace=None, out=None):
     ws, nbytes = _workspace(L.dflash_head_topk, before, (_stream(h.device),), h.device, workspace)
     _check(L.dflash_head_topk(*before, _ptr(ws), ctypes.byref(nbytes), _stream(h.device)),
            "dflash_head_topk")
+    return tv, ti
+
+
+def head_topk_noalloc(h, W, K=16, out=None):
+    """head_topk through the entry point that allocates nothing (the library's
+    static per-GPU scratch array); out=(top_val, top_idx) may be preallocated."""
+    _need(h, torch.bfloat16, "h", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    M, D = h.shape
+    V = W.shape[0]
+    if W.shape[1] != D:
+        raise DFlashError("W must be [V][D] with the same D as h")
+    if out is None:
+        tv = torch.empty((M, K), dtype=torch.float32, device=h.device)
+        ti = torch.empty((M, K), dtype=torch.int32, device=h.device)
+    else:
+        tv, ti = out
+    _check(lib().dflash_head_topk_noalloc(_ptr(h), _ptr(W), M, D, V, K, _ptr(tv), _ptr(ti), _stream(h.device)),
+           "dflash_head_topk_noalloc")
     return tv, ti
 
 

@@ -16,6 +16,9 @@ int launch_conv2tap_proj(const uint16_t*, const uint16_t*, uint16_t*, int64_t, i
 int launch_head_topk(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*, void*,
                      hipStream_t);
 size_t head_workspace_bytes(int64_t M, int64_t V);
+size_t head_static_scratch_bytes();
+int launch_head_topk_static(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*,
+                            hipStream_t);
 int launch_select_path(const float*, const int32_t*, const int32_t*, const float*, const float*, int, int, int64_t,
                        int, int32_t*, int32_t*, float*, void*, hipStream_t);
 size_t select_workspace_bytes(int B, int P, bool anchored);
@@ -125,9 +128,9 @@ int dflash_conv2tap_proj(const uint16_t* x, const uint16_t* w_tap, uint16_t* y, 
     return launch_conv2tap_proj(x, w_tap, y, n_seq, T, D, (hipStream_t)stream);
 }
 
-int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,
-                     float* top_val, int32_t* top_idx, void* workspace, size_t* workspace_bytes,
-                     void* stream) {
+// Argument checks shared by the head entry points (no HIP call).
+static int head_checks(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,
+                       float* top_val, int32_t* top_idx) {
     if (!h || !W || !top_val || !top_idx) return DFLASH_ERR_INVALID;
     if (M < 1 || D < 8 || D % 8 != 0 || D > 65536 || V < 1) return DFLASH_ERR_INVALID;
     if (K != 16) return DFLASH_ERR_UNSUPPORTED;
@@ -138,16 +141,34 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
         overlap(top_idx, nout, h, (size_t)M * D * 2) || overlap(top_val, nout, W, (size_t)V * D * 2) ||
         overlap(top_idx, nout, W, (size_t)V * D * 2))
         return DFLASH_ERR_INVALID;
+    return DFLASH_OK;
+}
+
+int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,
+                     float* top_val, int32_t* top_idx, void* workspace, size_t* workspace_bytes,
+                     void* stream) {
+    int st = head_checks(h, W, M, D, V, K, top_val, top_idx);
+    if (st != DFLASH_OK) return st;
     bool query = false;
-    int st = workspace_check(workspace, workspace_bytes, head_workspace_bytes(M, V), &query);
+    st = workspace_check(workspace, workspace_bytes, head_workspace_bytes(M, V), &query);
     if (st != DFLASH_OK || query) return st;
-    const size_t nws = *workspace_bytes;
+    const size_t nws = *workspace_bytes, nout = (size_t)M * K * 4;
     if (overlap(workspace, nws, h, (size_t)M * D * 2) || overlap(workspace, nws, W, (size_t)V * D * 2) ||
         overlap(workspace, nws, top_val, nout) || overlap(workspace, nws, top_idx, nout))
         return DFLASH_ERR_INVALID;
     st = check_device();
     if (st != DFLASH_OK) return st;
     return launch_head_topk(h, W, M, D, V, top_val, top_idx, workspace, (hipStream_t)stream);
+}
+
+int dflash_head_topk_noalloc(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D, int64_t V, int32_t K,
+                             float* top_val, int32_t* top_idx, void* stream) {
+    int st = head_checks(h, W, M, D, V, K, top_val, top_idx);
+    if (st != DFLASH_OK) return st;
+    if (head_workspace_bytes(M, V) > head_static_scratch_bytes()) return DFLASH_ERR_WORKSPACE;
+    st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_head_topk_static(h, W, M, D, V, top_val, top_idx, (hipStream_t)stream);
 }
 
 // Draws of the sampled-path selector (on = false: the max-sum selector).

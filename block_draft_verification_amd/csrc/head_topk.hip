@@ -1261,6 +1261,51 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
     return launch_status();
 }
 
+// ------------------------------------------------ allocation-free variant
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid hipMalloc): the partial lists live in a file-scope
+// device array instead of a caller workspace.  Every GPU holds its own copy
+// from module load until the process ends; calls on one GPU share it, so
+// calls that overlap in time on one GPU race on it (enqueue them on one
+// stream).  Nothing in it needs clearing: the GEMM writes every partial entry
+// the merge reads, and the merge writes every candidate the rank step reads.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+size_t head_static_scratch_bytes() { return kStaticScratchBytes; }
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+// The array's address on the current device, resolved once per device with
+// that device current (the array's name in host code is only a stand-in).
+static void* static_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) {
+            g_scratch_ptr[dev] = p;
+        } else {
+            (void)hipGetLastError();  // leave no sticky error for a later launch check
+            g_scratch_ptr[dev] = nullptr;
+        }
+    });
+    return g_scratch_ptr[dev];
+}
+
+// Caller has checked head_workspace_bytes(M, V) <= kStaticScratchBytes.
+int launch_head_topk_static(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, float* top_val,
+                            int32_t* top_idx, hipStream_t stream) {
+    if (head_workspace_bytes(M, V) > kStaticScratchBytes) return DFLASH_ERR_WORKSPACE;
+    void* ws = static_scratch();
+    if (!ws) return DFLASH_ERR_LAUNCH;
+    return launch_head_topk(h, W, M, D, V, top_val, top_idx, ws, stream);
+}
+
 // The same GEMMs with the softmax-statistics epilogue: rec [M][ceil(V/16)]
 // float2 (tile maximum, tile sum of exp((z - m) * inv_tau)); no merge.
 size_t head_stats_bytes(int64_t M, int64_t V) { return (size_t)M * ((V + 15) / 16) * 8; }

@@ -148,6 +148,24 @@ int dflash_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int32_t D,
                      void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * dflash_head_topk without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and requirements as
+ * dflash_head_topk; its scratch memory (the partial candidate lists) is a
+ * 16 MiB device array inside the library, one per GPU, held from the first
+ * use on that GPU until the process ends.  A size whose partial lists need
+ * more than 16 MiB (dflash_head_topk's workspace query reports the bytes)
+ * returns DFLASH_ERR_WORKSPACE before anything is enqueued; every M up to
+ * 65536 fits at V <= 262144.  The first call on a device resolves the array's
+ * address there (make it outside graph capture).  All calls on one GPU share
+ * the array: calls that may overlap in time on one GPU race, so enqueue them
+ * on one stream.  Allocates nothing, ever.
+ */
+int dflash_head_topk_noalloc(const uint16_t* h, const uint16_t* W, int64_t M,
+                             int32_t D, int64_t V, int32_t K, float* top_val,
+                             int32_t* top_idx, void* stream);
+
+/*
  * Pair selector: one coherent path through the P x K candidate lattice.
  * Source: tamsi.dev, section "L'idee, sans le papier" (a pair selector of
  * about 2 M parameters chooses a coherent path among good candidates);

@@ -116,6 +116,27 @@ def test_head_validation_and_workspace():
 
 
 @needs_lib
+def test_head_noalloc_validation():
+    """The allocation-free head checks like dflash_head_topk and rejects sizes
+    whose partial lists exceed its 16 MiB static scratch, before any HIP call."""
+    L = dfl.lib()
+    f = L.dflash_head_topk_noalloc
+    assert f(NULL, A[1], 7, 5120, 151936, 16, A[2], A[3], NULL) == INVALID
+    assert f(A[0], A[1], 7, 5120, 151936, 8, A[2], A[3], NULL) == UNSUPPORTED
+    assert f(A[0], A[1], 7, 5121, 151936, 16, A[2], A[3], NULL) == INVALID
+    assert f(A[0], A[1], 7, 5120, 151936, 16, A[0], A[3], NULL) == INVALID       # output aliases h
+    # 2^18 rows need 32 MiB of partial lists: rejected on size
+    need = ws_query(L.dflash_head_topk, A[0], A[1], 1 << 18, 256, 4096, 16, A[2], A[3])[1]
+    assert need > 16 << 20
+    assert f(A[0], A[1], 1 << 18, 256, 4096, 16, A[2], A[3], NULL) == WORKSPACE
+    # every M up to 65536 fits at V <= 262144
+    for M, V in ((65536, 4096), (65536, 262144), (224, 151936), (480, 262144), (7, 151936)):
+        assert ws_query(L.dflash_head_topk, A[0], A[1], M, 256, V, 16, A[2], A[3])[1] <= 16 << 20
+    if not torch.cuda.is_available():
+        assert f(A[0], A[1], 7, 5120, 151936, 16, A[2], A[3], NULL) == DEVICE
+
+
+@needs_lib
 def test_select_validation():
     f = dfl.lib().dflash_select_path
     n = ctypes.c_size_t(0)
