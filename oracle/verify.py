@@ -154,13 +154,25 @@ def verify_sample(logits, draft, temperature, seed, request_id, pos0,
 
 
 def _edge_margin(weights, target):
-    """Distance of an inverse-CDF target from its nearest bin edge, over the mass."""
-    c = np.cumsum(weights)
-    total = c[-1] if c[-1] > 0 else 1.0
-    k = int(np.searchsorted(c, target, side="right"))
-    lo = c[k - 1] if k > 0 else 0.0
-    hi = c[k] if k < c.size else math.inf
-    return min(abs(target - lo), abs(hi - target)) / total
+    """Distance, over the total mass, of an inverse-CDF target from the nearest
+    point where ``inverse_cdf`` would return another token.
+
+    Those points are the cumulative masses c[j] strictly between 0 and the
+    total: targets are never negative, and a target at or past the total falls
+    back to the last token of non-zero weight, which is also the token just
+    below the total.  So 0 and the total are not boundaries, and a zero-weight
+    bin adds none of its own (its c equals its predecessor's)."""
+    w = np.asarray(weights, dtype=np.float64)
+    c = np.cumsum(w)
+    total = c[-1] if c.size and c[-1] > 0 else 1.0
+    k = inverse_cdf(w, target)                 # the landing bin: positive weight
+    lo = c[k - 1] if k > 0 else 0.0            # its lower edge; c[k] its upper one
+    d = math.inf
+    if lo > 0.0:
+        d = min(d, abs(target - lo))
+    if c[k] < c[-1]:
+        d = min(d, abs(c[k] - target))
+    return d / total
 
 
 # ------------------------------------------------- top-k / top-p (nucleus)

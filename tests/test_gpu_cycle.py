@@ -252,6 +252,8 @@ def test_fused_target_head_cycle(dfl, dev):
                                                 inp["pos0"][g:], return_margins=True)
             same = (n[g:] == ref["n_emit"][g:]) & np.all(out[g:] == ref["out_tok"][g:], axis=1)
             assert np.all(same | (margin < 1e-5)), (name, np.nonzero(~same), margin[~same])
+            # about 1e-4 of requests lie that close to a boundary
+            assert (~same).sum() <= 2, (name, np.nonzero(~same))
 
 
 def _requests(inp, cfg, idx):

@@ -53,7 +53,8 @@ def test_matches_oracle(dfl, dev, B, T, D, V, grid):
                                                (16, 8, 1024, 20000, 1.3, 7.0)])
 def test_sample_fused_matches_oracle(dfl, dev, B, T, D, V, tau, boost):
     """Exact agreement with the sampler on exact logits, except for requests
-    whose decisions lie within the float32 error of a boundary (margin 1e-5)."""
+    whose decisions lie within the float32 error of a boundary (margin 1e-5),
+    and at most two of those."""
     from oracle.verify import verify_sample_hidden
     rng = np.random.default_rng(B + T + D + V)
     W = (0.02 * rng.standard_normal((V, D))).astype(np.float32)
@@ -73,4 +74,7 @@ def test_sample_fused_matches_oracle(dfl, dev, B, T, D, V, tau, boost):
     out, n = out.cpu().numpy(), n.cpu().numpy()
     same = (n == n0) & np.all(out == o0, axis=1)
     assert np.all(same | (margin < 1e-5)), (np.nonzero(~same), margin[~same])
-    assert same.mean() >= 0.75
+    # a request lies within 1e-5 of a boundary with probability about 1e-4
+    # (a few decisions per request, each within 1e-5 on either side), so more
+    # than two mismatches in a call would not be rounding
+    assert (~same).sum() <= 2, np.nonzero(~same)

@@ -130,3 +130,65 @@ def test_proj_exact_value_and_scale():
     assert torch.equal(y.view(torch.int16), bf16(y64.astype(np.float32)).view(torch.int16))
     assert np.all(np.abs(y64) <= scale)
     assert np.all(np.isfinite(y64))
+
+
+def test_proj_scale_hand_computed():
+    """S = 1, T = 2, D = 2 by hand: x_0 = (1, 2), x_1 = (3, -1); W_tap rows
+    (1, 0), (0, 1) give a = x, rows (2, 1), (1, -1) give b = (2 x_0 + x_1,
+    x_0 - x_1).  y_0 = a_0 x_0 = (1, 4) (no history); y_1 = a_1 x_1 + b_1 x_0 =
+    (9 + 5, 1 + 8).  scale = |a x| + |b x_prev| + 1e-3 (|x||W_a| |x| +
+    |x||W_b| |x_prev|)."""
+    from oracle.conv import conv2tap_proj
+    x = bf16([[[1, 2], [3, -1]]])
+    w = bf16([[1, 0], [0, 1], [2, 1], [1, -1]])
+    y, y64, scale = conv2tap_proj(x, w, return_exact=True)
+    assert np.array_equal(y64[0], [[1.0, 4.0], [14.0, 9.0]])
+    assert np.array_equal(y.float().numpy()[0], [[1.0, 4.0], [14.0, 9.0]])
+    np.testing.assert_allclose(scale[0], [[1.0 + 1e-3 * 1, 4.0 + 1e-3 * 4],
+                                          [14.0 + 1e-3 * (9 + 7), 9.0 + 1e-3 * (1 + 8)]], rtol=1e-15)
+
+
+def _proj_f32(x, w, reverse):
+    """The conv on projected taps evaluated in float32 with sequential sums in
+    a chosen order (the worst case for rounding), as a float32 kernel might."""
+    x32 = x.float().numpy().astype(np.float32)
+    w32 = w.float().numpy().astype(np.float32)
+    S, T, D = x32.shape
+    xr = x32.reshape(S * T, D)
+    acc = np.zeros((S * T, 2 * D), np.float32)
+    for d in (range(D - 1, -1, -1) if reverse else range(D)):
+        acc = (acc + xr[:, d:d + 1] * w32[:, d][None, :]).astype(np.float32)
+    a, b = acc[:, :D].reshape(S, T, D), acc[:, D:].reshape(S, T, D)
+    xp = np.zeros_like(x32)
+    xp[:, 1:] = x32[:, :-1]
+    return (a * x32 + b * xp).astype(np.float32).astype(np.float64)
+
+
+def test_proj_scale_bounds_float32_evaluation():
+    """Sequential float32 sums in either order stay within 1e-3 of the scale
+    of the exact value (the tolerance the GPU parity test uses)."""
+    from oracle.conv import conv2tap_proj
+    x = rand_bf16((3, 8, 512), 15)
+    w = (0.02 * torch.randn(1024, 512, generator=torch.Generator().manual_seed(16))).to(torch.bfloat16)
+    _, y64, scale = conv2tap_proj(x, w, return_exact=True)
+    for rev in (False, True):
+        err = np.abs(_proj_f32(x, w, rev) - y64)
+        assert np.all(err <= 1e-3 * scale)
+        assert err.max() > 0  # float32 really rounds here
+
+
+def test_proj_scale_covers_cancellation_inside_the_taps():
+    """a = 2^20 + 2^-8 - 2^20 cancels: float32 loses the 2^-8 entirely, so the
+    error is as large as the value itself; only the scale's second term (the
+    absolute sums inside the taps) covers it."""
+    from oracle.conv import conv2tap_proj
+    x = bf16([[[1, 1, 1], [1, 1, 1]]])
+    w = bf16([[2.0 ** 20, 2.0 ** -8, -2.0 ** 20], [0, 0, 0], [0, 0, 0],
+              [0, 0, 0], [0, 0, 0], [0, 0, 0]])
+    _, y64, scale = conv2tap_proj(x, w, return_exact=True)
+    assert y64[0, 0, 0] == 2.0 ** -8
+    err = np.abs(_proj_f32(x, w, False) - y64)
+    assert err[0, 0, 0] == 2.0 ** -8                       # float32 gives 0
+    first = np.abs(y64)                                     # |a x| + |b x_prev| (b = 0 here)
+    assert err[0, 0, 0] > 1e-3 * first[0, 0, 0]
+    assert np.all(err <= 1e-3 * scale)

@@ -2,6 +2,7 @@
 continuation; sampling against the target distribution (exact law on a grid
 of uniforms, chi-square on Philox draws) and its closed-form special cases."""
 
+import math
 import numpy as np
 import pytest
 from scipy import stats
@@ -344,3 +345,79 @@ def test_sample_from_hidden_states_equals_sampling_integer_logits():
     ref = verify_sample(z.astype(np.float64) * 0.25, d, 1.0, 8, rid, pos0)
     got = verify_sample_hidden(h * 0.5, W * 0.5, d, 1.0, 8, rid, pos0)
     assert np.array_equal(ref[0], got[0]) and np.array_equal(ref[1], got[1])
+
+
+# --- the admissibility helpers (distance of a decision from its boundary) ---
+
+def test_edge_margin_hand_computed():
+    """c = 1, 3, 6, 10: targets inside bins, on an edge, in the first and the
+    last bin; zero-weight bins; targets at or past the total."""
+    from oracle.verify import _edge_margin
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    assert _edge_margin(w, 4.5) == pytest.approx(0.15)     # bin 2: 1.5 to both edges
+    assert _edge_margin(w, 3.0) == 0.0                      # exactly on the edge 3
+    assert _edge_margin(w, 0.2) == pytest.approx(0.08)      # bin 0: 0 is no edge, 0.8 to 1
+    assert _edge_margin(w, 9.9) == pytest.approx(0.39)      # last bin: 10 is no edge, 3.9 to 6
+    assert _edge_margin(w, 10.0) == pytest.approx(0.4)      # past the total: falls back to bin 3
+    z = np.array([0.0, 2.0, 0.0, 0.0, 3.0])                 # c = 0, 2, 2, 2, 5
+    assert _edge_margin(z, 2.5) == pytest.approx(0.1)       # the only edge is 2
+    assert _edge_margin(z, 1.0) == pytest.approx(0.2)
+    assert _edge_margin(np.array([0.0, 0.0, 7.0]), 3.0) == math.inf   # one token can be drawn
+    assert _edge_margin(np.array([5.0, 0.0, 0.0]), 0.1) == math.inf
+
+
+def test_edge_margin_is_the_distance_to_a_change_of_token():
+    """Moving the target by less than the margin (times the mass) keeps the
+    drawn token; moving it by slightly more, one way or the other, changes it."""
+    from oracle.verify import _edge_margin, inverse_cdf
+    rng = np.random.default_rng(21)
+    for trial in range(300):
+        n = int(rng.integers(1, 12))
+        w = rng.random(n) * (rng.random(n) > 0.3)
+        if w.sum() == 0:
+            w[int(rng.integers(n))] = 1.0
+        tot = float(np.cumsum(w)[-1])
+        t = float(rng.random()) * tot
+        m = _edge_margin(w, t)
+        tok = inverse_cdf(w, t)
+        if m == math.inf:
+            assert np.count_nonzero(w) == 1
+            continue
+        step = m * tot
+        for f in (-0.99, 0.99):
+            if t + f * step >= 0:
+                assert inverse_cdf(w, t + f * step) == tok
+        moved = [inverse_cdf(w, t + f * step) for f in (-1.01, 1.01) if t + f * step >= 0]
+        assert any(v != tok for v in moved), (w, t, m)
+
+
+def test_cut_margin_hand_computed():
+    """e = 1, 1/2, 1/4, 1/8 (Zk = 1.875), nucleus bound top_p * Zk against the
+    masses before tokens 1, 2, 3 (1, 1.5, 1.75)."""
+    from oracle.verify import _cut_margin
+    row = np.log(np.array([1.0, 0.5, 0.25, 0.125]))
+    assert _cut_margin(row, 1.0, 4, 0.8) == 0.0                          # bound 1.5 = mass before token 2
+    assert _cut_margin(row, 1.0, 4, 0.7) == pytest.approx(0.1875 / 1.875)  # bound 1.3125
+    assert _cut_margin(row, 1.0, 2, 0.7) == pytest.approx(0.05 / 1.5)     # top-2: Zk 1.5, bound 1.05
+    assert _cut_margin(row, 1.0, 1, 0.5) == math.inf                       # one token: nothing to cut
+    # order and temperature: the same weights from a permuted row at tau = 2
+    perm = np.array([2, 0, 3, 1])
+    assert _cut_margin(2.0 * row[perm], 0.5, 4, 0.7) == pytest.approx(0.1)
+
+
+def test_cut_margin_is_the_distance_to_a_change_of_set():
+    """Moving top_p by less than the margin keeps the filtered set; by slightly
+    more in one direction or the other it changes."""
+    from oracle.verify import _cut_margin, filtered_set
+    rng = np.random.default_rng(22)
+    for trial in range(200):
+        V = int(rng.integers(2, 40))
+        row = rng.standard_normal(V) * 2.0
+        k = int(rng.integers(2, V + 1))
+        p = float(rng.uniform(0.2, 0.95))
+        m = _cut_margin(row, 1.0, k, p)
+        ids = filtered_set(row, 1.0, k, p)[0]
+        for f in (-0.99, 0.99):
+            assert np.array_equal(filtered_set(row, 1.0, k, p + f * m)[0], ids)
+        moved = [filtered_set(row, 1.0, k, p + f * m)[0] for f in (-1.01, 1.01) if 0 < p + f * m <= 1]
+        assert any(not np.array_equal(x, ids) for x in moved), (row, k, p, m)
