@@ -104,11 +104,45 @@ def _need(t, dtype, name, dims=None):
         raise DFlashError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
 
 
+def _same_device(what, *ts):
+    """Every tensor argument of one call must live on the same GPU."""
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise DFlashError(f"{what}: tensors on several devices {sorted(map(str, devs))}")
+
+
+def _out(t, dtype, shape, device, name):
+    """A caller-supplied output: the C ABI cannot see tensor sizes, so its
+    dtype, exact shape, device and contiguity are checked here, before any
+    launch."""
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise DFlashError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise DFlashError(f"{name} must be on {device}, got {t.device}")
+    return t
+
+
+def _outs(out, specs, device):
+    """out=None allocates every output; else out is a tuple checked against
+    specs [(dtype, shape, name), ...]."""
+    if out is None:
+        return tuple(torch.empty(shape, dtype=dt, device=device) for dt, shape, _ in specs)
+    if not isinstance(out, (tuple, list)) or len(out) != len(specs):
+        raise DFlashError(f"out must be a tuple of {len(specs)} tensors")
+    return tuple(_out(t, dt, shape, device, name) for t, (dt, shape, name) in zip(out, specs))
+
+
 def _workspace(fn, args_before, args_after, device, workspace):
-    """Query the workspace size with a NULL workspace, then allocate if needed."""
+    """Query the workspace size with a NULL workspace, then allocate if needed
+    (a caller's workspace must be a contiguous uint8 tensor on the device)."""
     need = ctypes.c_size_t(0)
     _check(fn(*args_before, None, ctypes.byref(need), *args_after), fn.__name__ + " (workspace query)")
     n = max(int(need.value), 16)
+    if workspace is not None:
+        _need(workspace, torch.uint8, "workspace")
+        if workspace.device != device:
+            raise DFlashError(f"workspace must be on {device}, got {workspace.device}")
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(n, dtype=torch.uint8, device=device)
     return workspace, ctypes.c_size_t(workspace.numel())
@@ -118,13 +152,13 @@ def conv2tap(x, taps, out=None):
     """x bf16 [S][T][D], taps bf16 [S][T][2D] -> y bf16 [S][T][D]."""
     _need(x, torch.bfloat16, "x")
     _need(taps, torch.bfloat16, "taps")
+    _same_device("conv2tap", x, taps)
     D = x.shape[-1]
     T = x.shape[-2]
     S = x.numel() // (T * D)
     if taps.shape[-1] != 2 * D or taps.numel() != 2 * x.numel():
         raise DFlashError("taps must be [..., T, 2*D] matching x")
-    y = torch.empty_like(x) if out is None else out
-    _need(y, torch.bfloat16, "out")
+    y = torch.empty_like(x) if out is None else _out(out, torch.bfloat16, x.shape, x.device, "out")
     _check(lib().dflash_conv2tap(_ptr(x), _ptr(taps), _ptr(y), S, T, D, _stream(x.device)),
            "dflash_conv2tap")
     return y
@@ -134,13 +168,13 @@ def conv2tap_proj(x, w_tap, out=None):
     """x bf16 [S][T][D], w_tap bf16 [2D][D] -> y bf16 [S][T][D]."""
     _need(x, torch.bfloat16, "x")
     _need(w_tap, torch.bfloat16, "w_tap")
+    _same_device("conv2tap_proj", x, w_tap)
     D = x.shape[-1]
     T = x.shape[-2]
     S = x.numel() // (T * D)
     if tuple(w_tap.shape) != (2 * D, D):
         raise DFlashError("w_tap must be [2*D][D]")
-    y = torch.empty_like(x) if out is None else out
-    _need(y, torch.bfloat16, "out")
+    y = torch.empty_like(x) if out is None else _out(out, torch.bfloat16, x.shape, x.device, "out")
     _check(lib().dflash_conv2tap_proj(_ptr(x), _ptr(w_tap), _ptr(y), S, T, D, _stream(x.device)),
            "dflash_conv2tap_proj")
     return y
@@ -154,11 +188,8 @@ def head_topk(h, W, K=16, workspace=None, out=None):
     V = W.shape[0]
     if W.shape[1] != D:
         raise DFlashError("W must be [V][D] with the same D as h")
-    if out is None:
-        tv = torch.empty((M, K), dtype=torch.float32, device=h.device)
-        ti = torch.empty((M, K), dtype=torch.int32, device=h.device)
-    else:
-        tv, ti = out
+    _same_device("head_topk", h, W)
+    tv, ti = _outs(out, [(torch.float32, (M, K), "top_val"), (torch.int32, (M, K), "top_idx")], h.device)
     L = lib()
     before = (_ptr(h), _ptr(W), M, D, V, K, _ptr(tv), _ptr(ti))
     ws, nbytes = _workspace(L.dflash_head_topk, before, (_stream(h.device),), h.device, workspace)
@@ -176,11 +207,8 @@ def head_topk_noalloc(h, W, K=16, out=None):
     V = W.shape[0]
     if W.shape[1] != D:
         raise DFlashError("W must be [V][D] with the same D as h")
-    if out is None:
-        tv = torch.empty((M, K), dtype=torch.float32, device=h.device)
-        ti = torch.empty((M, K), dtype=torch.int32, device=h.device)
-    else:
-        tv, ti = out
+    _same_device("head_topk_noalloc", h, W)
+    tv, ti = _outs(out, [(torch.float32, (M, K), "top_val"), (torch.int32, (M, K), "top_idx")], h.device)
     _check(lib().dflash_head_topk_noalloc(_ptr(h), _ptr(W), M, D, V, K, _ptr(tv), _ptr(ti), _stream(h.device)),
            "dflash_head_topk_noalloc")
     return tv, ti
@@ -202,12 +230,9 @@ def select_path(top_val, top_idx, F_l, F_r, workspace=None, out=None, anchor=Non
         _need(anchor, torch.int32, "anchor", 1)
         if anchor.numel() != B:
             raise DFlashError("anchor must hold one id per request")
-    if out is None:
-        rank = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
-        tok = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
-        score = torch.empty((B,), dtype=torch.float32, device=top_val.device)
-    else:
-        rank, tok, score = out
+    _same_device("select_path", top_val, top_idx, F_l, F_r, anchor)
+    rank, tok, score = _outs(out, [(torch.int32, (B, P), "path_rank"), (torch.int32, (B, P), "path_tok"),
+                                   (torch.float32, (B,), "path_score")], top_val.device)
     L = lib()
     if anchor is None:
         fn, name = L.dflash_select_path, "dflash_select_path"
@@ -229,11 +254,8 @@ def verify_greedy(logits, draft, workspace=None, out=None):
     B, T, V = logits.shape
     if tuple(draft.shape) != (B, T - 1):
         raise DFlashError("draft must be [B][T-1]")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
-        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
-    else:
-        o, n = out
+    _same_device("verify_greedy", logits, draft)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
     L = lib()
     before = (_ptr(logits), _ptr(draft), B, T, V, _ptr(o), _ptr(n))
     ws, nbytes = _workspace(L.dflash_verify_greedy, before, (_stream(logits.device),), logits.device,
@@ -253,11 +275,8 @@ def verify_sample(logits, draft, temperature, seed, request_id, pos0, workspace=
     B, T, V = logits.shape
     if tuple(draft.shape) != (B, T - 1) or request_id.numel() != B or pos0.numel() != B:
         raise DFlashError("shape mismatch in verify_sample")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
-        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
-    else:
-        o, n = out
+    _same_device("verify_sample", logits, draft, request_id, pos0)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
     L = lib()
     before = (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(seed) & (2**64 - 1),
               _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
@@ -287,12 +306,9 @@ def select_path_sampled(top_val, top_idx, F_l, F_r, seed, request_id, pos0, anch
         _need(anchor, torch.int32, "anchor", 1)
         if anchor.numel() != B:
             raise DFlashError("anchor must hold one id per request")
-    if out is None:
-        rank = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
-        tok = torch.empty((B, P), dtype=torch.int32, device=top_val.device)
-        q = torch.empty((B, P, K), dtype=torch.float64, device=top_val.device)
-    else:
-        rank, tok, q = out
+    _same_device("select_path_sampled", top_val, top_idx, F_l, F_r, anchor, request_id, pos0)
+    rank, tok, q = _outs(out, [(torch.int32, (B, P), "path_rank"), (torch.int32, (B, P), "path_tok"),
+                               (torch.float64, (B, P, K), "path_q")], top_val.device)
     L = lib()
     before = (_ptr(top_val), _ptr(top_idx), None if anchor is None else _ptr(anchor), _ptr(F_l), _ptr(F_r), B, P,
               K, V, r, int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(rank), _ptr(tok), _ptr(q))
@@ -317,11 +333,8 @@ def verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id,
     if (tuple(draft.shape) != (B, T - 1) or tuple(q_idx.shape) != (B, T - 1, 16)
             or tuple(q_prob.shape) != (B, T - 1, 16) or request_id.numel() != B or pos0.numel() != B):
         raise DFlashError("shape mismatch in verify_sample_q")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
-        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
-    else:
-        o, n = out
+    _same_device("verify_sample_q", logits, draft, q_idx, q_prob, request_id, pos0)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
     L = lib()
     before = (_ptr(logits), _ptr(draft), _ptr(q_idx), _ptr(q_prob), B, T, V, float(temperature),
               int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
@@ -344,11 +357,8 @@ def verify_greedy_fused(h_t, W, draft, workspace=None, out=None):
     V = W.shape[0]
     if M != B * T or W.shape[1] != D:
         raise DFlashError("shape mismatch in verify_greedy_fused")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=h_t.device)
-        n = torch.empty((B,), dtype=torch.int32, device=h_t.device)
-    else:
-        o, n = out
+    _same_device("verify_greedy_fused", h_t, W, draft)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], h_t.device)
     L = lib()
     before = (_ptr(h_t), _ptr(W), _ptr(draft), B, T, D, V, _ptr(o), _ptr(n))
     ws, nbytes = _workspace(L.dflash_verify_greedy_fused, before, (_stream(h_t.device),), h_t.device, workspace)
@@ -373,11 +383,8 @@ def verify_sample_fused(h_t, W, draft, temperature, seed, request_id, pos0, work
     V = W.shape[0]
     if M != B * T or W.shape[1] != D or request_id.numel() != B or pos0.numel() != B:
         raise DFlashError("shape mismatch in verify_sample_fused")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=h_t.device)
-        n = torch.empty((B,), dtype=torch.int32, device=h_t.device)
-    else:
-        o, n = out
+    _same_device("verify_sample_fused", h_t, W, draft, request_id, pos0)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], h_t.device)
     L = lib()
     before = (_ptr(h_t), _ptr(W), _ptr(draft), B, T, D, V, float(temperature), int(seed) & (2**64 - 1),
               _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
@@ -399,11 +406,8 @@ def verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_
     B, T, V = logits.shape
     if tuple(draft.shape) != (B, T - 1) or request_id.numel() != B or pos0.numel() != B:
         raise DFlashError("shape mismatch in verify_sample_topkp")
-    if out is None:
-        o = torch.empty((B, T), dtype=torch.int32, device=logits.device)
-        n = torch.empty((B,), dtype=torch.int32, device=logits.device)
-    else:
-        o, n = out
+    _same_device("verify_sample_topkp", logits, draft, request_id, pos0)
+    o, n = _outs(out, [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
     L = lib()
     before = (_ptr(logits), _ptr(draft), B, T, V, float(temperature), int(top_k), float(top_p),
               int(seed) & (2**64 - 1), _ptr(request_id), _ptr(pos0), _ptr(o), _ptr(n))
@@ -428,11 +432,41 @@ def _bound(fn, args, what):
     return call
 
 
+def _bind_ws(workspace, device):
+    _need(workspace, torch.uint8, "workspace")
+    if workspace.device != device:
+        raise DFlashError(f"workspace must be on {device}, got {workspace.device}")
+
+
+def _bind_sample_checks(logits, draft, request_id, pos0, out_tok, n_emit, workspace):
+    _need(logits, torch.float32, "logits", 3)
+    B, T, V = logits.shape
+    _outs((draft, request_id, pos0), [(torch.int32, (B, T - 1), "draft"), (torch.int64, (B,), "request_id"),
+                                      (torch.int64, (B,), "pos0")], logits.device)
+    _outs((out_tok, n_emit), [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
+    _bind_ws(workspace, logits.device)
+
+
+def _bind_fused_checks(h_t, W, draft, out_tok, n_emit, workspace):
+    _need(h_t, torch.bfloat16, "h_t", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(draft, torch.int32, "draft", 2)
+    B, P = draft.shape
+    if h_t.shape[0] != B * (P + 1) or W.shape[1] != h_t.shape[1]:
+        raise DFlashError("shape mismatch in fused verification")
+    _same_device("fused verification", h_t, W, draft)
+    _outs((out_tok, n_emit), [(torch.int32, (B, P + 1), "out_tok"), (torch.int32, (B,), "n_emit")], h_t.device)
+    _bind_ws(workspace, h_t.device)
+
+
 def bind_conv2tap_proj(x, w_tap, y):
     _need(x, torch.bfloat16, "x")
     _need(w_tap, torch.bfloat16, "w_tap")
-    _need(y, torch.bfloat16, "y")
+    _out(y, torch.bfloat16, x.shape, x.device, "y")
     D, T = x.shape[-1], x.shape[-2]
+    if tuple(w_tap.shape) != (2 * D, D):
+        raise DFlashError("w_tap must be [2*D][D]")
+    _same_device("conv2tap_proj", x, w_tap)
     S = x.numel() // (T * D)
     return _bound(lib().dflash_conv2tap_proj, (_ptr(x), _ptr(w_tap), _ptr(y), S, T, D, _stream(x.device)),
                   "dflash_conv2tap_proj")
@@ -441,8 +475,11 @@ def bind_conv2tap_proj(x, w_tap, y):
 def bind_conv2tap(x, taps, y):
     _need(x, torch.bfloat16, "x")
     _need(taps, torch.bfloat16, "taps")
-    _need(y, torch.bfloat16, "y")
+    _out(y, torch.bfloat16, x.shape, x.device, "y")
     D, T = x.shape[-1], x.shape[-2]
+    if taps.shape[-1] != 2 * D or taps.numel() != 2 * x.numel():
+        raise DFlashError("taps must be [..., T, 2*D] matching x")
+    _same_device("conv2tap", x, taps)
     S = x.numel() // (T * D)
     return _bound(lib().dflash_conv2tap, (_ptr(x), _ptr(taps), _ptr(y), S, T, D, _stream(x.device)),
                   "dflash_conv2tap")
@@ -452,6 +489,11 @@ def bind_head_topk(h, W, top_val, top_idx, workspace):
     _need(h, torch.bfloat16, "h", 2)
     _need(W, torch.bfloat16, "W", 2)
     M, D = h.shape
+    if W.shape[1] != D:
+        raise DFlashError("W must be [V][D] with the same D as h")
+    _same_device("head_topk", h, W)
+    _outs((top_val, top_idx), [(torch.float32, (M, 16), "top_val"), (torch.int32, (M, 16), "top_idx")], h.device)
+    _bind_ws(workspace, h.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_head_topk,
                   (_ptr(h), _ptr(W), M, D, W.shape[0], top_val.shape[-1], _ptr(top_val), _ptr(top_idx),
@@ -459,8 +501,18 @@ def bind_head_topk(h, W, top_val, top_idx, workspace):
 
 
 def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score, workspace, anchor=None):
+    _need(top_val, torch.float32, "top_val", 3)
+    _need(top_idx, torch.int32, "top_idx", 3)
+    _need(F_l, torch.float32, "F_l", 2)
+    _need(F_r, torch.float32, "F_r", 2)
     B, P, K = top_val.shape
     V, r = F_l.shape
+    if tuple(F_r.shape) != (V, r) or tuple(top_idx.shape) != (B, P, K):
+        raise DFlashError("shape mismatch in select_path")
+    _same_device("select_path", top_val, top_idx, F_l, F_r, anchor)
+    _outs((rank, tok, score), [(torch.int32, (B, P), "path_rank"), (torch.int32, (B, P), "path_tok"),
+                               (torch.float32, (B,), "path_score")], top_val.device)
+    _bind_ws(workspace, top_val.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     if anchor is None:
         return _bound(lib().dflash_select_path,
@@ -475,7 +527,11 @@ def bind_select_path(top_val, top_idx, F_l, F_r, rank, tok, score, workspace, an
 
 
 def bind_verify_greedy(logits, draft, out_tok, n_emit, workspace):
+    _need(logits, torch.float32, "logits", 3)
     B, T, V = logits.shape
+    _out(draft, torch.int32, (B, T - 1), logits.device, "draft")
+    _outs((out_tok, n_emit), [(torch.int32, (B, T), "out_tok"), (torch.int32, (B,), "n_emit")], logits.device)
+    _bind_ws(workspace, logits.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_greedy,
                   (_ptr(logits), _ptr(draft), B, T, V, _ptr(out_tok), _ptr(n_emit), _ptr(workspace),
@@ -483,6 +539,7 @@ def bind_verify_greedy(logits, draft, out_tok, n_emit, workspace):
 
 
 def bind_verify_sample(logits, draft, temperature, seed, request_id, pos0, out_tok, n_emit, workspace):
+    _bind_sample_checks(logits, draft, request_id, pos0, out_tok, n_emit, workspace)
     B, T, V = logits.shape
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_sample,
@@ -493,6 +550,7 @@ def bind_verify_sample(logits, draft, temperature, seed, request_id, pos0, out_t
 
 def bind_verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, request_id, pos0, out_tok, n_emit,
                              workspace):
+    _bind_sample_checks(logits, draft, request_id, pos0, out_tok, n_emit, workspace)
     B, T, V = logits.shape
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_sample_topkp,
@@ -503,8 +561,19 @@ def bind_verify_sample_topkp(logits, draft, temperature, top_k, top_p, seed, req
 
 def bind_select_path_sampled(top_val, top_idx, F_l, F_r, seed, request_id, pos0, rank, tok, q, workspace,
                              anchor=None):
+    _need(top_val, torch.float32, "top_val", 3)
+    _need(top_idx, torch.int32, "top_idx", 3)
+    _need(F_l, torch.float32, "F_l", 2)
+    _need(F_r, torch.float32, "F_r", 2)
     B, P, K = top_val.shape
     V, r = F_l.shape
+    if tuple(F_r.shape) != (V, r) or tuple(top_idx.shape) != (B, P, K):
+        raise DFlashError("shape mismatch in select_path_sampled")
+    _outs((request_id, pos0), [(torch.int64, (B,), "request_id"), (torch.int64, (B,), "pos0")], top_val.device)
+    _same_device("select_path_sampled", top_val, top_idx, F_l, F_r, anchor)
+    _outs((rank, tok, q), [(torch.int32, (B, P), "path_rank"), (torch.int32, (B, P), "path_tok"),
+                           (torch.float64, (B, P, K), "path_q")], top_val.device)
+    _bind_ws(workspace, top_val.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_select_path_sampled,
                   (_ptr(top_val), _ptr(top_idx), None if anchor is None else _ptr(anchor), _ptr(F_l), _ptr(F_r), B,
@@ -514,7 +583,10 @@ def bind_select_path_sampled(top_val, top_idx, F_l, F_r, seed, request_id, pos0,
 
 def bind_verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, request_id, pos0, out_tok, n_emit,
                          workspace):
+    _bind_sample_checks(logits, draft, request_id, pos0, out_tok, n_emit, workspace)
     B, T, V = logits.shape
+    _outs((q_idx, q_prob), [(torch.int32, (B, T - 1, 16), "q_idx"), (torch.float64, (B, T - 1, 16), "q_prob")],
+          logits.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_sample_q,
                   (_ptr(logits), _ptr(draft), _ptr(q_idx), _ptr(q_prob), B, T, V, float(temperature),
@@ -523,6 +595,7 @@ def bind_verify_sample_q(logits, draft, q_idx, q_prob, temperature, seed, reques
 
 
 def bind_verify_greedy_fused(h_t, W, draft, out_tok, n_emit, workspace):
+    _bind_fused_checks(h_t, W, draft, out_tok, n_emit, workspace)
     B, P = draft.shape
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_greedy_fused,
@@ -531,7 +604,9 @@ def bind_verify_greedy_fused(h_t, W, draft, out_tok, n_emit, workspace):
 
 
 def bind_verify_sample_fused(h_t, W, draft, temperature, seed, request_id, pos0, out_tok, n_emit, workspace):
+    _bind_fused_checks(h_t, W, draft, out_tok, n_emit, workspace)
     B, P = draft.shape
+    _outs((request_id, pos0), [(torch.int64, (B,), "request_id"), (torch.int64, (B,), "pos0")], h_t.device)
     nbytes = ctypes.c_size_t(workspace.numel())
     return _bound(lib().dflash_verify_sample_fused,
                   (_ptr(h_t), _ptr(W), _ptr(draft), B, P + 1, h_t.shape[1], W.shape[0], float(temperature),
