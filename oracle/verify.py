@@ -161,10 +161,14 @@ def _edge_margin(weights, target):
     total: targets are never negative, and a target at or past the total falls
     back to the last token of non-zero weight, which is also the token just
     below the total.  So 0 and the total are not boundaries, and a zero-weight
-    bin adds none of its own (its c equals its predecessor's)."""
+    bin adds none of its own (its c equals its predecessor's).  With no mass
+    at all there is no draw (a residual is empty only when the drafted token
+    holds all of the mass, and then it is always accepted): no boundary."""
     w = np.asarray(weights, dtype=np.float64)
     c = np.cumsum(w)
-    total = c[-1] if c.size and c[-1] > 0 else 1.0
+    if not c.size or not c[-1] > 0:
+        return math.inf
+    total = c[-1]
     k = inverse_cdf(w, target)                 # the landing bin: positive weight
     lo = c[k - 1] if k > 0 else 0.0            # its lower edge; c[k] its upper one
     d = math.inf

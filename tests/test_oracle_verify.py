@@ -199,9 +199,14 @@ def test_topkp_single_token_is_greedy(top_k, top_p):
     L, d, rng = _greedyish(11)
     for seed in (0, 5, 77):
         rid = rng.integers(0, 2**40, L.shape[0])
-        o, n = verify_sample_topkp(L, d, 1.0, top_k, top_p, seed, rid, rng.integers(0, 2**30, L.shape[0]))
+        p0 = rng.integers(0, 2**30, L.shape[0])
+        o, n = verify_sample_topkp(L, d, 1.0, top_k, top_p, seed, rid, p0)
         o0, n0 = verify_greedy(L, d)
         assert np.array_equal(o, o0) and np.array_equal(n, n0)
+        # the margins see empty residuals (an accepted one-token set): the
+        # decisions are the same, and only the acceptance tests bound them
+        o1, n1, mg = verify_sample_topkp(L, d, 1.0, top_k, top_p, seed, rid, p0, return_margins=True)
+        assert np.array_equal(o1, o) and np.array_equal(n1, n) and np.all(mg >= 0)
 
 
 def test_topkp_worked_nucleus():
@@ -364,6 +369,10 @@ def test_edge_margin_hand_computed():
     assert _edge_margin(z, 1.0) == pytest.approx(0.2)
     assert _edge_margin(np.array([0.0, 0.0, 7.0]), 3.0) == math.inf   # one token can be drawn
     assert _edge_margin(np.array([5.0, 0.0, 0.0]), 0.1) == math.inf
+    # no mass (the residual of a filtered set that is only the drafted
+    # token): nothing is drawn, so no boundary either
+    assert _edge_margin(np.zeros(3), 0.0) == math.inf
+    assert _edge_margin(np.zeros(0), 0.0) == math.inf
 
 
 def test_edge_margin_is_the_distance_to_a_change_of_token():
