@@ -243,7 +243,12 @@ def make_sets(torch, cfg, inp, max_sets):
 
 
 def head_kernels(cfg):
-    gemm = "head_skinny2_kernel" if cfg.M <= 16 else "head_wide_kernel"
+    if cfg.M <= 16:
+        gemm = "head_skinny2_kernel"
+    elif cfg.M <= 64:
+        gemm = "head_wide_kernel"
+    else:
+        gemm = "head_mfma_kernel"
     return f"dflash_head_topk call = {gemm} + head_merge_kernel (HIP events around the call)"
 
 

@@ -811,6 +811,460 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
     }
 }
 
+// ------------------------------------------- wide GEMM, W straight into registers
+// head_mfma_kernel (M > 64): a workgroup of 4 wavefronts (one per SIMD, up to
+// 512 registers each) owns an M-block of 16*MT rows of h and a contiguous,
+// balanced range of 16-row vocabulary tiles, walked in strips of 64*NT rows.
+// Wavefront w owns every row of the block and the strip's tiles w, w + 4,
+// w + 8, ... (interleaved, so a partial last strip spreads over all four);
+// its 16*MT x 16*NT float32 accumulators (4*MT*NT registers, at most 240) stay
+// in AGPRs for the whole strip, updated in place by v_mfma_f32_16x16x32_bf16
+// (register-only inline asm, so the accumulators are never renamed or copied).
+//
+// W is read by one wavefront only, so it goes straight from memory into
+// registers in the MFMA operand layout: per chunk of 64 hidden columns, lane
+// (r, g) (r = lane % 16, g = lane / 16) loads bytes 16 g and 64 + 16 g of its
+// row's 128-byte line (k = 8 g and 32 + 8 g: the two k-steps), the two halves
+// back to back.  Chunk c+3 is requested as chunk c starts, so three chunks
+// are in flight beyond the one being multiplied: under a full streaming load
+// HBM answers in ~3.5 us, which takes ~100 KB in flight per CU (an LDS ring
+// that deep would not fit next to h).
+// h is shared by the four wavefronts: per chunk its 16*MT rows x 128 bytes go
+// straight into a 4-stage LDS ring with buffer_load_dwordx4 ... lds (no
+// register staging; rows unpadded, 16-byte pieces permuted piece ^ (row & 6),
+// which keeps fragment reads free of bank conflicts).  Each A fragment read
+// from LDS feeds NT MFMAs; reads run R - 1 fragments ahead, the last ones of a
+// chunk already reading the next chunk.  One barrier per chunk, between its
+// two k-steps: h chunk c+1 has landed in every wavefront's part and chunk
+// c-1's stage is no longer read, so it is refilled with chunk c+3 (two chunks
+// of lookahead) while the second k-step runs.  The instruction order is
+// fixed with scheduling barriers; the vmcnt waits count on it.
+//
+// After each strip the running top-16 lists (in LDS for the whole call)
+// absorb the strip's logits (strip_topk).
+template <int MT, int NT>
+struct MfmaCfg {
+    static constexpr int MB = 16 * MT;            // rows of h per workgroup
+    static constexpr int NB = 64 * NT;            // W rows per strip (4 wavefronts x 16 NT)
+    static constexpr int KC = 64;                 // hidden columns per chunk (128 bytes per row)
+    static constexpr int HST = 4;                 // h ring stages
+    static constexpr int HSTAGE = MB * 128;
+    static constexpr int HI = MB / 8;             // h DMA instructions (8 rows of 128 bytes) per chunk
+    static constexpr int HPW = (HI + 3) / 4;      // per wavefront (extra ones fill a spare block)
+    // A fragments in flight: a ring of R register sets, R dividing the 2 MT
+    // fragments of a chunk (so a fragment's slot does not depend on the
+    // chunk) and at least 5 (4 read ahead of the one multiplied)
+    static constexpr int ring_size() {
+        for (int r = 5; r <= 2 * MT; ++r)
+            if ((2 * MT) % r == 0) return r;
+        return 2 * MT;
+    }
+    static constexpr int R = ring_size();
+    static constexpr int PF = R - 1;              // A fragments read ahead
+    static constexpr size_t SPARE = (size_t)HST * HSTAGE;  // 1 KB target of the extra DMAs
+    static constexpr size_t LISTS = SPARE + 1024;           // lists, thresholds, slot counters
+    static constexpr size_t LDS = LISTS + (size_t)MB * (kTopK * 8 + 8);
+    static constexpr int CAP = 32;                // candidate keys per row and round
+    static_assert((size_t)MB * CAP * 8 <= SPARE && (size_t)MB * 64 * 4 <= SPARE,
+                  "candidates and seed lists fit in the drained ring");
+    static_assert(LDS <= 160 * 1024, "LDS per workgroup");
+    static_assert(MT * NT * 4 <= 240 && NT <= 8, "accumulators fit in the AGPRs");
+    static_assert(PF <= MT && (2 * MT) % R == 0, "prefetch distance within a k-step");
+};
+
+// waitcnt with only vmcnt = n (0 <= n < 64); lgkmcnt and expcnt not waited
+#define DFLASH_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (7 << 4) | (0xF << 8))
+
+// One strip's K loop.  NTP <= NT: only the wavefront's first NTP column tiles
+// are multiplied (a partial last strip; the others keep zeros and are not
+// admitted); rows past M are multiplied as zeros and never admitted either.
+template <int MT, int NT, int NTP>
+__device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, const __amdgpu_buffer_rsrc_t wsrc,
+                                           int D, int nK, int wave, int lane_in, floatx4 (&acc)[MT][NT]) {
+    using C = MfmaCfg<MT, NT>;
+    constexpr int HPW = C::HPW;
+    extern __shared__ __align__(16) unsigned char smem[];
+    // Per-lane offsets are computed here, per strip, from an opaque copy of
+    // the lane id: kept live across the top-16 epilogue they would be spilled,
+    // and every reload before a DMA would wait for all loads in flight.
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    const int ln = lane & 15, lg = lane >> 4;
+    int hoff[HPW], hdst[HPW], woff[NTP];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+        const int j = wave + 4 * u;  // h DMA instruction: rows 8 j .. 8 j + 7
+        hoff[u] = j < C::HI ? (j * 8 + (lane >> 3)) * D * 2 + (((lane & 7) ^ ((lane >> 3) & 6)) * 16) : kOffNone;
+        hdst[u] = j < C::HI ? j * 1024 : -1;
+    }
+#pragma unroll
+    for (int t = 0; t < NTP; ++t) woff[t] = (16 * (wave + 4 * t) + ln) * D * 2 + lg * 16;
+    // DMA: lane l writes bytes 16 l of its instruction's 1 KB (8 rows of 128
+    // bytes): row l / 8, position l % 8, holding logical piece (l % 8) ^
+    // ((l / 8) & 6); pieces past D (a ragged last chunk) load zeros
+    const int dcol = ((lane & 7) ^ ((lane >> 3) & 6)) * 8;
+    // fragment reads: row ln of a 16-row tile, logical piece 4 s + lg
+    const int fo0 = ln * 128 + ((0 + lg) ^ (ln & 6)) * 16;
+    const int fo1 = ln * 128 + ((4 + lg) ^ (ln & 6)) * 16;
+
+    auto issue_h = [&](int c) __attribute__((always_inline)) {
+        const bool live = c < nK && c * C::KC + dcol < D;
+        const int soff = c < nK ? c * 128 : 0;
+        const int st = (c % C::HST) * C::HSTAGE;
+#pragma unroll
+        for (int u = 0; u < HPW; ++u)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                hsrc, (__attribute__((address_space(3))) void*)(smem + (hdst[u] < 0 ? (int)C::SPARE : st + hdst[u])),
+                16, live ? hoff[u] : kOffNone, soff, 0, 0);
+    };
+    u32x4 wq[4][NTP][2];  // W chunks in flight: slot c % 4
+    auto issue_w = [&](u32x4 (&slot)[NTP][2], int c) __attribute__((always_inline)) {
+        const int soff = c < nK ? c * 128 : 0;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bool live = c < nK && c * C::KC + 32 * s + 8 * lg < D;
+#pragma unroll
+            for (int t = 0; t < NTP; ++t)
+                slot[t][s] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? woff[t] + 64 * s : kOffNone, soff, 0);
+        }
+    };
+    auto barrier = []() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+    // A fragment k of a chunk: k-step k / MT, tile k % MT
+    auto frag = [&](int c, int k) __attribute__((always_inline)) {
+        const int s = k / MT, i = k % MT;
+        return *reinterpret_cast<const u32x4*>(smem + (c % C::HST) * C::HSTAGE + (16 * i) * 128 + (s ? fo1 : fo0));
+    };
+    u32x4 fa[C::R];
+    // the MFMAs of A fragment k (in fa[k % R]) of a chunk with its W slot,
+    // reading fragment k + PF (of this chunk or, past its end, of the next)
+    // (past the last chunk the reads land in a stage that holds zeros or a
+    // chunk already multiplied: in bounds, never used; reading them
+    // unconditionally keeps the loop free of branches, whose joins would
+    // drain the fragment reads in flight)
+    auto frag_step = [&](const u32x4 (&slot)[NTP][2], int c, int k) __attribute__((always_inline)) {
+        const int s = k / MT, i = k % MT;
+        const u32x4 a = fa[k % C::R];
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+            asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][t]) : "v"(a), "v"(slot[t][s]));
+            if (t == 0) {
+                const int kn = k + C::PF;
+                fa[kn % C::R] = kn < 2 * MT ? frag(c, kn) : frag(c + 1, kn - 2 * MT);  // slot (kn - 2 MT) % R
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto chunk = [&](u32x4 (&slot)[NTP][2], u32x4 (&nslot)[NTP][2], int c) __attribute__((always_inline)) {
+        // W chunk c+3 into the slot that chunk c-1 multiplied (its MFMAs have
+        // read their operands long before the data returns)
+        __builtin_amdgcn_sched_barrier(0);
+        issue_w(nslot, c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 0
+#pragma unroll
+        for (int k = 0; k < MT; ++k) frag_step(slot, c, k);
+        // h chunk c+1 landed in every part (after it were issued W c+2, h c+2
+        // and W c+3); chunk c-1's stage is no longer read
+        DFLASH_WAIT_VM(4 * NTP + HPW);
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_h(c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 1 (its last reads are the next chunk's first fragments)
+#pragma unroll
+        for (int k = MT; k < 2 * MT; ++k) frag_step(slot, c, k);
+    };
+    // prologue: W0 h0 W1 h1 W2 h2 in flight (the steady-state order, every
+    // group fenced); h chunk 0 landed everywhere; its first fragments read
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wq[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_h(0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wq[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_h(1);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wq[2], 2);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_h(2);
+    __builtin_amdgcn_sched_barrier(0);
+    DFLASH_WAIT_VM(4 * NTP + 2 * HPW);
+    barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < C::PF; ++k) fa[k] = frag(0, k);
+    for (int c = 0; c < nK; c += 4) {
+        chunk(wq[0], wq[3], c);
+        chunk(wq[1], wq[0], c + 1);
+        chunk(wq[2], wq[1], c + 2);
+        chunk(wq[3], wq[2], c + 3);
+    }
+    DFLASH_WAIT_VM(0);
+    barrier();
+    // the last MFMAs' results must be written before anything reads the AGPRs
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+// The running top-16 lists of head_mfma_kernel (LDS).
+struct StripLists {
+    uint64_t* list;   // [MB][16] descending keys (kEmptyKey until filled), for the whole call
+    float* thr;       // [MB] value of each row's 16th entry (-inf until 16 exist), or the seed
+    int* cnt;         // [MB] candidate slots reserved this round (may pass CAP)
+    uint64_t* cand;   // [MB][CAP] candidate keys (the drained ring)
+    float* seed;      // [MB][4][16] per-wavefront sorted lane maxima (first strip; aliases cand)
+};
+
+// One strip's logits, still in the accumulators, into the running lists.
+// acc[i][t][q] is row 16 i + 4 (lane / 16) + q of the block and vocabulary
+// column col0 + 16 (wave + 4 t) + lane % 16.
+//  * First strip: each row's threshold starts at the 16th largest of its 64
+//    lane maxima (4 wavefronts x 16 lanes): 64 distinct entries, so no more
+//    than the row's 16th best.  Per wavefront the 16 lane maxima of a row are
+//    sorted in its 16-lane group, then one group merges the four sorted lists.
+//  * Filter: a value is a candidate iff it is at or above its row's threshold
+//    (the 16th entry's value; ties at it are offered and sorted out by the
+//    merge); values below it can never enter the list.  Candidates go to a
+//    per-row buffer of CAP keys: each lane reserves a run of slots per row
+//    with one LDS atomic (the reservations of a fragment row issued together,
+//    so a round costs one LDS round trip per fragment row, not per value).
+//  * Merge: 16-lane group g takes rows g, g + 16, ...; for each that received
+//    candidates it sorts them 16 at a time and merges them into the row's
+//    descending list (bitonic); the threshold becomes the new 16th value.
+//    Candidates that found a full buffer stay pending for another round.
+template <int MT, int NT>
+__device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const StripLists& sl, int wave, int lane_in,
+                                           int rows_blk, int64_t col0, int nt_act, int64_t V, bool first) {
+    constexpr int CAP = MfmaCfg<MT, NT>::CAP;
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    const int ln = lane & 15, lg = lane >> 4;
+    // Per-lane LDS bases (local address space); everything else in an address
+    // is a compile-time offset (a ds instruction's immediate), so no per-row
+    // address lives in a register.  The empty asm keeps each base from being
+    // folded back into per-row addresses.
+    //  filter: rows 16 i + 4 lg + q;  merge: group g = 4 wave + lg, rows g + 16 j
+    const int g = wave * 4 + lg;
+    auto base = [](auto* p) __attribute__((always_inline)) {
+        using T = std::remove_pointer_t<decltype(p)>;
+        auto* q = (__attribute__((address_space(3))) T*)p;
+        asm volatile("" : "+v"(q));
+        return q;
+    };
+    auto* thr_l = base(sl.thr + 4 * lg);
+    auto* cnt_l = base(sl.cnt + 4 * lg);
+    auto* cand_l = base(sl.cand + 4 * lg * CAP);
+    auto* cand_g = base(sl.cand + g * CAP + ln);
+    auto* list_g = base(sl.list + g * kTopK + ln);
+    auto* cnt_g = base(sl.cnt + g);
+    auto* thr_g = base(sl.thr + g);
+    // accumulators are read where they are used, straight from their AGPRs:
+    // copies kept in VGPRs across the rounds would not fit
+    auto rd = [](const float& x) __attribute__((always_inline)) {
+        float v;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+        return v;
+    };
+    auto thr_at = [&](int i) { return *(const __attribute__((address_space(3))) floatx4*)(thr_l + 16 * i); };
+    auto cnt_at = [&](int i, int q) { return (int*)(cnt_l + 16 * i + q); };
+    auto cand_at = [&](int i, int q) { return cand_l + (16 * i + q) * CAP; };
+
+    // pending bits: bit 4 t + q of pend[i] <=> acc[i][t][q] is still to be offered
+    uint32_t tbits = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+        if (t < nt_act && col0 + 16 * (wave + 4 * t) + ln < V) tbits |= 0xFu << (4 * t);
+    uint32_t pend[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        uint32_t qb = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (16 * i + 4 * lg + q < rows_blk) qb |= 0x1111u << q;
+        pend[i] = tbits & qb;
+    }
+    if (first) {
+        // seeds: [row][wavefront][16] sorted lane maxima
+        auto* seed_l = base(sl.seed + (4 * lg * 4 + wave) * 16 + ln);
+        auto* seed_g = base(sl.seed + g * 64 + ln);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    if (pend[i] & (1u << (4 * t + q))) m = fmaxf(m, rd(acc[i][t][q]));
+                m = sort16_desc_f32(m, ln);
+                seed_l[(16 * i + q) * 64] = m;
+            }
+            // one fragment row at a time: interleaved, the rows' sorting
+            // networks would hold every accumulator in a register at once
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int j = 0; j < MT; ++j) {
+            const auto* b = seed_g + j * 16 * 64;  // row g + 16 j, lane ln
+            // the four lists reversed where a bitonic merge needs it: lane ln
+            // reads entry 15 - ln of lists 1 and 3 (offset 15 - 2 ln from its own)
+            float x = fmaxf(b[0], b[16 + 15 - 2 * ln]);  // top 16 of wavefronts 0 and 1 (bitonic)
+            float y = fmaxf(b[32], b[48 + 15 - 2 * ln]);
+            x = merge16_desc_f32(x, ln);
+            y = merge16_desc_f32(y, ln);
+            float z = fmaxf(x, dpp_f32v<kDppX15>(y));  // top 16 of all four (bitonic)
+            z = fminf(z, dpp_f32v<kDppX1>(z));
+            z = fminf(z, dpp_f32v<kDppX2>(z));
+            z = fminf(z, xor4_f32(z, ln));
+            z = fminf(z, dpp_f32v<kDppX8>(z));
+            if (ln == 0) thr_g[16 * j] = z;
+        }
+        __syncthreads();  // the seeds are read; the candidates reuse their memory
+    }
+    while (true) {
+        // thresholds read one fragment row ahead
+        floatx4 tn = thr_at(0);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            const floatx4 t4 = tn;
+            if (i + 1 < MT) tn = thr_at(i + 1);
+            if (__ballot(pend[i] != 0) == 0) continue;
+            const float tq[4] = {t4[0], t4[1], t4[2], t4[3]};
+            uint32_t m = 0;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (rd(acc[i][t][q]) >= tq[q]) m |= 1u << (4 * t + q);
+            m &= pend[i];
+            pend[i] = m;  // below the threshold: never again
+            // one reservation per lane and row (row 16 i + 4 lg + q): a run of
+            // slots as long as the lane's candidates for that row; the four
+            // reservations are issued back to back
+            int base[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = __builtin_popcount(m & (0x1111u << q));
+                base[q] = n ? atomicAdd(cnt_at(i, q), n) : CAP;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                int slot = base[q];
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const uint32_t bit = 1u << (4 * t + q);
+                    if ((m & bit) && slot < CAP) {
+                        cand_at(i, q)[slot] = rank_key(rd(acc[i][t][q]), (int)(col0 + 16 * (wave + 4 * t) + ln));
+                        pend[i] &= ~bit;  // offered; a candidate past the buffer stays pending
+                    }
+                    slot += (m & bit) ? 1 : 0;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        // 16-lane group g merges rows g, g + 16, ...: those with candidates
+        int nrow[MT];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) nrow[j] = cnt_g[16 * j];
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+            const int n = min(nrow[j], CAP);
+            if (n == 0) continue;
+            auto* lst = list_g + 16 * kTopK * j;
+            const auto* cnd = cand_g + 16 * CAP * j;
+            uint64_t lk = *lst;
+            for (int c0 = 0; c0 < n; c0 += 16) {
+                uint64_t ck = c0 + ln < n ? cnd[c0] : kEmptyKey;
+                ck = sort16<false>(ck, ln);
+                lk = lk > ck ? lk : ck;
+                lk = merge16_desc(lk, ln);
+            }
+            *lst = lk;
+            if (ln == kTopK - 1) thr_g[16 * j] = key_value(lk);
+            if (ln == 0) cnt_g[16 * j] = 0;
+        }
+        int any = 0;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) any |= pend[i] != 0;
+        if (!__syncthreads_or(any)) break;
+    }
+}
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, int64_t n_tiles, int S,
+                      int n_mb, float* __restrict__ part_val, int* __restrict__ part_idx) {
+    // (h and W are deliberately not __restrict__: loads from restrict read-only
+    // memory may be moved across the barrier asm, which would break the issue
+    // order that the vmcnt waits count on)
+    using C = MfmaCfg<MT, NT>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    // workgroup -> (M-block, slot): the M-blocks of one slot are dispatched
+    // back to back on the same XCD so they share the slot's W rows in L2.
+    const int L = blockIdx.x;
+    const int xcd = L & 7;
+    const int kq = L >> 3;
+    const int mb = kq % n_mb;
+    const int slot = (kq / n_mb) * 8 + xcd;
+    if (slot >= S) return;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int64_t m0 = (int64_t)mb * C::MB;
+    const int rows_blk = (int)min<int64_t>(C::MB, M - m0);
+    const int nK = (D + C::KC - 1) / C::KC;
+    // Rows past the block or the strip read as zero (the resources end there).
+    const __amdgpu_buffer_rsrc_t hsrc = make_rsrc(h + m0 * D, (int64_t)rows_blk * D * 2);
+
+    StripLists sl;
+    unsigned char* lp = smem + C::LISTS;
+    sl.list = reinterpret_cast<uint64_t*>(lp);
+    sl.thr = reinterpret_cast<float*>(lp + C::MB * kTopK * 8);
+    sl.cnt = reinterpret_cast<int*>(sl.thr + C::MB);
+    sl.cand = reinterpret_cast<uint64_t*>(smem);  // the drained ring (epilogue only)
+    sl.seed = reinterpret_cast<float*>(smem);
+    for (int e = tid; e < C::MB * kTopK; e += 256) sl.list[e] = kEmptyKey;
+    for (int e = tid; e < C::MB; e += 256) {
+        sl.thr[e] = -INFINITY;
+        sl.cnt[e] = 0;
+    }
+    __syncthreads();
+
+    const int64_t t_begin = (int64_t)slot * n_tiles / S, t_end = (int64_t)(slot + 1) * n_tiles / S;
+    for (int64_t t0 = t_begin; t0 < t_end; t0 += C::NB / 16) {
+        const int64_t col0 = t0 * 16;
+        const int tiles_here = (int)min<int64_t>(C::NB / 16, t_end - t0);
+        const int64_t rows_here = min<int64_t>((int64_t)tiles_here * 16, V - col0);
+        const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(W + col0 * D, rows_here * D * 2);
+        const int nt_act = max(0, min(NT, (tiles_here - wave + 3) / 4));
+        floatx4 acc[MT][NT];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int t = 0; t < NT; ++t) acc[i][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // every wavefront runs the same loop (barriers); a partial strip
+        // multiplies only as many column tiles as the busiest wavefront holds
+        const int need = (tiles_here + 3) / 4;
+        if (need > NT / 2)
+            mfma_strip<MT, NT, NT>(hsrc, wsrc, D, nK, wave, lane, acc);
+        else if (need > 1)
+            mfma_strip<MT, NT, NT / 2>(hsrc, wsrc, D, nK, wave, lane, acc);
+        else
+            mfma_strip<MT, NT, 1>(hsrc, wsrc, D, nK, wave, lane, acc);
+        strip_topk<MT, NT>(acc, sl, wave, lane, rows_blk, col0, nt_act, V, t0 == t_begin);
+        __syncthreads();  // the ring (epilogue scratch) is refilled by the next strip
+    }
+    for (int e = tid; e < rows_blk * kTopK; e += 256) {
+        const int r = e / kTopK, k = e % kTopK;
+        const int64_t o = ((m0 + r) * S + slot) * kTopK + k;
+        part_val[o] = key_value(sl.list[e]);
+        part_idx[o] = key_id(sl.list[e]);
+    }
+}
+
 // ---------------------------------------------------------------- merge
 // G workgroups of 10 wavefronts per row (G = 1 for many rows, up to 5 for a
 // few, so that the exact re-scoring is spread over more CUs).
@@ -1102,7 +1556,8 @@ __global__ __launch_bounds__(64 * kRankRows) void head_rank_kernel(int64_t M, in
 // ------------------------------------------------------------------ host
 namespace {
 
-enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3, kWide64 = 4 };
+enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3, kWide64 = 4, kMfma128 = 5, kMfma224 = 6,
+                   kMfma240 = 7 };
 
 struct HeadPlan {
     HeadVariant variant;
@@ -1134,6 +1589,25 @@ struct WideVariant {
     }
 };
 
+// One instantiation of head_mfma_kernel with its launch.
+template <int MT, int NT>
+struct MfmaVariant {
+    using Cfg = MfmaCfg<MT, NT>;
+    static const void* fn() { return reinterpret_cast<const void*>(&head_mfma_kernel<MT, NT>); }
+    static void set_attr() {
+        (void)hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+    }
+    static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
+                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
+        const int grid = (S + 7) / 8 * 8 * n_mb;
+        hipLaunchKernelGGL((head_mfma_kernel<MT, NT>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M, D, V,
+                           n_tiles, S, n_mb, pv, pi);
+    }
+};
+using Mfma128 = MfmaVariant<8, 4>;   // M-blocks of 128 rows, 256-row strips
+using Mfma224 = MfmaVariant<14, 4>;  // M-blocks of 224 rows, 256-row strips
+using Mfma240 = MfmaVariant<15, 4>;  // M-blocks of 240 rows, 256-row strips
+
 // two workgroups of four wavefronts per CU (measured faster than one of eight)
 constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWaves = 4, kSkinnyWG = 512;
 using SkinnyL = SkinnyLds<kSkinnyNT, kSkinnyKS, kSkinnyWaves>;
@@ -1152,7 +1626,9 @@ using Wide128W = WideVariant<4, 4, 2, 2, true, 4, true>;
 using Wide64 = WideVariant<2, 2, 2, 4, true, 4>;
 constexpr int kCUs = 256;
 
-HeadPlan head_plan(int64_t M, int64_t V) {
+// stats: the plan of the softmax-statistics GEMMs (fused sampling), which
+// run on the LDS-staged wide kernels
+HeadPlan head_plan(int64_t M, int64_t V, bool stats = false) {
     HeadPlan p{};
     p.n_tiles = (V + 15) / 16;
     // merge workgroups per row: spread the re-scoring of few rows over more CUs
@@ -1165,21 +1641,35 @@ HeadPlan head_plan(int64_t M, int64_t V) {
         p.S = (int)std::min<int64_t>(kSkinnyWG, want);
         return p;
     }
-    // the M-block size that pads M the least (224-row blocks win ties: fewer
-    // of them read W)
-    const int64_t pad128 = (M + 127) / 128 * 128, pad224 = (M + 223) / 224 * 224;
-    if (M > 128 && pad224 <= pad128) {
-        p.variant = kWide224;
-        p.mb_rows = Wide224::Cfg::MB;
-    } else if (M > 128) {
-        p.variant = kWide128W;
-        p.mb_rows = Wide128W::Cfg::MB;
+    if (stats && M > 64) {
+        const int64_t pad128 = (M + 127) / 128 * 128, pad224 = (M + 223) / 224 * 224;
+        if (M > 128 && pad224 <= pad128) {
+            p.variant = kWide224;
+            p.mb_rows = Wide224::Cfg::MB;
+        } else if (M > 128) {
+            p.variant = kWide128W;
+            p.mb_rows = Wide128W::Cfg::MB;
+        } else {
+            p.variant = kWide128;
+            p.mb_rows = Wide128::Cfg::MB;
+        }
     } else if (M <= 64) {
         p.variant = kWide64;
         p.mb_rows = Wide64::Cfg::MB;
     } else {
-        p.variant = kWide128;
-        p.mb_rows = Wide128::Cfg::MB;
+        // the M-block size that pads M the least (larger blocks win ties:
+        // fewer of them read W)
+        const int64_t pad128 = (M + 127) / 128 * 128, pad224 = (M + 223) / 224 * 224, pad240 = (M + 239) / 240 * 240;
+        if (pad240 <= pad224 && pad240 <= pad128) {
+            p.variant = kMfma240;
+            p.mb_rows = Mfma240::Cfg::MB;
+        } else if (pad224 <= pad128) {
+            p.variant = kMfma224;
+            p.mb_rows = Mfma224::Cfg::MB;
+        } else {
+            p.variant = kMfma128;
+            p.mb_rows = Mfma128::Cfg::MB;
+        }
     }
     p.n_mb = (int)((M + p.mb_rows - 1) / p.mb_rows);
     // one workgroup per CU (the chunk tile takes most of the LDS)
@@ -1215,6 +1705,9 @@ static void set_head_attrs() {
         Wide224::set_attr();
         Wide128W::set_attr();
         Wide64::set_attr();
+        Mfma128::set_attr();
+        Mfma224::set_attr();
+        Mfma240::set_attr();
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&head_merge_kernel),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLists * kTopK * 8);
     });
@@ -1242,6 +1735,15 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
             break;
         case kWide128W:
             Wide128W::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            break;
+        case kMfma128:
+            Mfma128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            break;
+        case kMfma224:
+            Mfma224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            break;
+        case kMfma240:
+            Mfma240::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
         default:
             Wide224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
@@ -1313,7 +1815,7 @@ size_t head_stats_bytes(int64_t M, int64_t V) { return (size_t)M * ((V + 15) / 1
 int launch_head_stats(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, double inv_tau,
                       float2* rec, hipStream_t stream) {
     set_head_attrs();
-    const HeadPlan p = head_plan(M, V);
+    const HeadPlan p = head_plan(M, V, true);
     const TileStats st{rec, (V + 15) / 16, (float)(inv_tau * 1.4426950408889634)};
     switch (p.variant) {
         case kSkinny:

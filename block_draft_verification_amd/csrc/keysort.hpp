@@ -73,6 +73,40 @@ __device__ __forceinline__ uint64_t merge16_desc(uint64_t k, int li) {
     return k;
 }
 
+// The same networks on plain float32 values (no ids), for thresholds.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32v(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float xor4_f32(float x, int li) {
+    const float up = dpp_f32v<0x104>(x);
+    const float dn = dpp_f32v<0x114>(x);
+    return (li & 4) ? dn : up;
+}
+__device__ __forceinline__ float cxf(float k, float p, bool keep_max) { return keep_max ? fmaxf(k, p) : fminf(k, p); }
+// Descending bitonic sort of one value per lane over each 16-lane row.
+__device__ __forceinline__ float sort16_desc_f32(float k, int li) {
+    k = cxf(k, dpp_f32v<kDppX1>(k), (li & 1) == 0);
+    k = cxf(k, dpp_f32v<kDppX3>(k), (li & 2) == 0);
+    k = cxf(k, dpp_f32v<kDppX1>(k), (li & 1) == 0);
+    k = cxf(k, dpp_f32v<kDppX7>(k), (li & 4) == 0);
+    k = cxf(k, dpp_f32v<kDppX2>(k), (li & 2) == 0);
+    k = cxf(k, dpp_f32v<kDppX1>(k), (li & 1) == 0);
+    k = cxf(k, dpp_f32v<kDppX15>(k), (li & 8) == 0);
+    k = cxf(k, xor4_f32(k, li), (li & 4) == 0);
+    k = cxf(k, dpp_f32v<kDppX2>(k), (li & 2) == 0);
+    k = cxf(k, dpp_f32v<kDppX1>(k), (li & 1) == 0);
+    return k;
+}
+// Sort a bitonic sequence of 16 values (one per lane of a row) descending.
+__device__ __forceinline__ float merge16_desc_f32(float k, int li) {
+    k = cxf(k, dpp_f32v<kDppX8>(k), (li & 8) == 0);
+    k = cxf(k, xor4_f32(k, li), (li & 4) == 0);
+    k = cxf(k, dpp_f32v<kDppX2>(k), (li & 2) == 0);
+    k = cxf(k, dpp_f32v<kDppX1>(k), (li & 1) == 0);
+    return k;
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
     const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m);
     const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m);
