@@ -22,7 +22,9 @@ import os
 import torch  # loads the HIP runtime the library binds to
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdflash.so")
+# DFLASH_LIB names another build of the same library (the host-sanitized one
+# for the C-ABI checks); by default the one next to this file.
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(_HERE, "libdflash.so")
 
 _c_i32, _c_i64, _c_u64, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
 _p, _psz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)

@@ -23,18 +23,41 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+# The host-sanitized variant (AddressSanitizer + UndefinedBehaviorSanitizer on
+# the host code only; the device code is built as usual).  It links the shared
+# sanitizer runtime, which a process must preload (SAN_RUNTIME) to load it.
+SAN_OUT = os.path.join(HERE, "libdflash_san.so")
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-shared-libsan", "-O1",
+]
+
+
+def san_runtime():
+    """Path of the shared AddressSanitizer runtime of hipcc's host compiler."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose=False, sanitize=False):
+    out, bdir = (SAN_OUT, SAN_BUILD) if sanitize else (OUT, BUILD)
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".", "_") + ".o")
-        cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, src.replace(".", "_") + ".o")
+        cmd = [HIPCC] + FLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         _run(cmd, verbose)
         objs.append(obj)
-    tmp = OUT + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, OUT)
-    return OUT
+    tmp = out + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC"] + extra + ["-o", tmp] + objs, verbose)
+    os.replace(tmp, out)
+    return out
 
 
 def _run(cmd, verbose):
@@ -49,4 +72,4 @@ def _run(cmd, verbose):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
