@@ -161,6 +161,27 @@ def test_stagewise_stress_context_copy(dfl, dev):
     assert res["n_emit"].float().mean().item() > 3.0
 
 
+@pytest.mark.parametrize("name", ["c3_b8", "c4_b32", "c5_stress"])
+def test_full_config_every_row(dfl, dev, name):
+    """The full-size configurations end to end: generator -> GPU cycle against
+    generator -> the oracle's whole cycle (float64) on host copies of the same
+    inputs; conv on every sequence, the head on every row, then paths,
+    emitted tokens and lengths of every request, all bit for bit."""
+    cfg = get_config(name)
+    inp = make_cycle_inputs(cfg, device=dev)
+    print(f"[{name}] GPU cycle", flush=True)
+    res = gpu_cycle(dfl, inp, cfg)
+    host = {k: (v.cpu() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    print(f"[{name}] oracle cycle", flush=True)
+    ref = run_cycle(host, cfg.B, cfg.T, verify=cfg.verify)
+    for l in range(cfg.L):
+        assert torch.equal(res["y"][l].cpu().view(torch.int16), ref["y"][l].view(torch.int16)), l
+    assert np.array_equal(res["top_idx"].cpu().numpy(), ref["top_idx"])
+    assert np.array_equal(res["top_val"].cpu().numpy(), ref["top_val"])
+    for k in ("path_rank", "path_tok", "path_score", "out_tok", "n_emit"):
+        assert np.array_equal(res[k].cpu().numpy(), ref[k]), k
+
+
 def gpu_cycle_sampled_path(dfl, inp, cfg):
     """The cycle with the sampled requests' path drawn (select_path_sampled)
     and verified against its proposals (verify_sample_q)."""
