@@ -11,6 +11,10 @@ are timed twice: launched eagerly (with per-stage events) and replayed from
 one captured HIP graph per input set (the reported value; the replayed outputs
 are checked to equal the eager ones).
 
+By default the headline is the batch-32 workload (c4_b32); batch 1 (c2_b1)
+and batch 8 (c3_b8) follow as sub-records of the same line, each with its own
+roofline, oracle timing and parity.
+
 Prints ONE JSON line on stdout; diagnostics go to stderr.
 """
 
@@ -48,7 +52,13 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--config", default="c2_b1", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--config", default="c4_b32", choices=sorted(WORKLOAD_TEXT),
+                    help="the headline workload (default c4_b32: batch 32)")
+    ap.add_argument("--sub-configs", default=None,
+                    help="comma-separated workloads measured after the headline and reported in its "
+                         "'sub_records' key (default: c2_b1,c3_b8 with the default headline, none otherwise; "
+                         "'none' for none)")
+    ap.add_argument("--sub-steps", type=int, default=200, help="timed steps of each sub-record")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="bound on the oracle's timed CPU work")
@@ -259,7 +269,9 @@ def head_roofline(cfg, head_us):
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     t = head_us * 1e-6
     traffic = stored_traffic(cfg)
-    if ai < ridge:
+    # batched heads (M > 64 rows: the MFMA kernel) are reported against the
+    # bf16 MFMA peak, with the byte-side fraction beside it
+    if ai < ridge and cfg.M <= 64:
         ach = bytes_ / t / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -419,15 +431,45 @@ def main():
               "(--gpus must be 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import block_draft_verification_amd as dfl
-    from workload import get_config, make_cycle_inputs
 
     dfl.lib()
+    subs = args.sub_configs
+    if subs is None:
+        subs = "c2_b1,c3_b8" if args.config == "c4_b32" and not variant_flags(args) else "none"
+    subs = [] if subs == "none" else [c for c in subs.split(",") if c]
+    for c in subs:
+        if c not in WORKLOAD_TEXT:
+            sys.exit(f"unknown sub-config {c}")
+    rec = run_config(args, torch, dfl, args.config, args.steps, args.cpu_seconds)
+    if subs:
+        rec["sub_records"] = {}
+        for c in subs:
+            torch.cuda.empty_cache()
+            sub = run_config(args, torch, dfl, c, args.sub_steps, min(args.cpu_seconds, 10.0))
+            rec["sub_records"][c] = {k: sub[k] for k in ("value", "unit", "ms_per_step", "steps", "config",
+                                                         "roofline", "cycle_roofline", "stages_us",
+                                                         "eager_cycles_per_s", "mean_n_emit", "cpu_baseline")
+                                     if k in sub}
+            if "parity_vs_oracle" in sub:
+                rec["sub_records"][c]["parity_vs_oracle"] = sub["parity_vs_oracle"]
+    print(json.dumps(rec), flush=True)
+
+
+def variant_flags(args):
+    return (args.sample_top_k > 0 or args.anchored or args.sampled_path or args.fused_target_head
+            or args.fused_tap_proj)
+
+
+def run_config(args, torch, dfl, name, steps, cpu_seconds):
+    """Measure one workload; returns its JSON record."""
+    import numpy as np
+    from workload import get_config, make_cycle_inputs
+
     dev = torch.device("cuda:0")
-    cfg = get_config(args.config, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
+    cfg = get_config(name, top_k=args.sample_top_k, top_p=args.sample_top_p, anchored=args.anchored,
                      sampled_path=args.sampled_path, fused_target_head=args.fused_target_head,
                      fused_tap_proj=args.fused_tap_proj)
     if cfg.fused_target_head and (cfg.sampled_path or cfg.top_k > 0):
@@ -449,23 +491,23 @@ def main():
 
     # per-stage events on the stream the kernels run on
     stream = torch.cuda.current_stream(dev)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         runner.run(i, evs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / args.steps
+    ms_per_step = ms_total / steps
     stage = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(4)] for e in evs]) * 1e3  # us
     cycle_us = np.array([e[0].elapsed_time(e[4]) for e in evs]) * 1e3
     head_us = float(stage[:, 1].mean())
-    log(f"[bench] {args.steps} cycles in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
+    log(f"[bench] {steps} cycles in {ms_total:.2f} ms (wall {wall * 1e3:.1f} ms): "
         f"{ms_per_step * 1e3:.1f} us/cycle; head {head_us:.1f} us")
 
     # outputs of one eager cycle on set 0, for the parity check
@@ -481,11 +523,11 @@ def main():
     g_start = torch.cuda.Event(enable_timing=True)
     g_end = torch.cuda.Event(enable_timing=True)
     g_start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         graphs[i % len(graphs)].replay()
     g_end.record(stream)
     torch.cuda.synchronize()
-    ms_graph = g_start.elapsed_time(g_end) / args.steps
+    ms_graph = g_start.elapsed_time(g_end) / steps
     graphs[0].replay()
     torch.cuda.synchronize()
     g_res = runner.outputs()
@@ -501,7 +543,7 @@ def main():
         "value": round(1e3 / ms_graph, 2),
         "unit": "cycles/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_graph, 5),
         "higher_is_better": True,
@@ -533,13 +575,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same inputs")
-        cb, parity = cpu_baseline(torch, cfg, inp, gpu_res, args.cpu_seconds)
+        cb, parity = cpu_baseline(torch, cfg, inp, gpu_res, cpu_seconds)
         rec["cpu_baseline"] = cb
         rec["parity_vs_oracle"] = parity
         log(f"[bench] oracle {cb['value']} cycles/s on {cb['cores']} threads; parity {parity}")
     else:
         rec["cpu_baseline"] = None
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 if __name__ == "__main__":

@@ -86,6 +86,72 @@ def test_sample_distribution_chi_square(dfl, dev):
     assert stats.chisquare(f_obs, f_exp * f_obs.sum() / f_exp.sum()).pvalue > 1e-3
 
 
+def _f32(x):
+    return float(np.float32(x))
+
+
+def _band_rows(seed, rid, pos, V, delta):
+    """Two crafted requests per sign of delta, each with T = 2 (one draft
+    slot, then the bonus row):
+    * 'accept': row 0 puts the draft d = 5 at p(d) = u_acc (1 + delta) (its
+      logit and the logit of token 7 tuned in float32; the rest 0), so the
+      acceptance test u_acc Z < e(d) sits inside the float32 band;
+    * 'draw': row 0 accepts surely (draft logit 40) and row 1 (the bonus)
+      puts the draw target u_res Z at (1 + delta) times a cumulative edge
+      (the weight of token 0 tuned; the rest 1)."""
+    from oracle.verify import uniforms
+    rows, drafts = [], []
+    for r, kind in zip(rid, ("accept", "draw")):
+        L = np.zeros((2, V), np.float32)
+        u_acc, _ = uniforms(seed, int(r), int(pos) + 1)
+        _, u_res = uniforms(seed, int(r), int(pos) + 2)
+        if kind == "accept":
+            p = u_acc * (1.0 + delta)
+            ld = _f32(np.log(p * (V - 1) / (1.0 - p)))
+            ex = np.exp(np.float64(ld)) / p - np.exp(np.float64(ld)) - (V - 2)
+            L[0, 5], L[0, 7] = ld, _f32(np.log(ex))
+        else:
+            L[0, 5] = 40.0
+            k = u_res * (1.0 + delta)
+            J = int(np.floor(k * (V - 1) - (1.0 - k)))
+            w = (k * (V - 1) - J) / (1.0 - k)
+            L[1, 0] = _f32(np.log(w))
+        rows.append(L)
+        drafts.append([5])
+    return np.stack(rows), np.array(drafts, np.int32)
+
+
+def test_sample_decisions_next_to_their_boundary(dfl, dev):
+    """Acceptance tests and draws placed between 1e-12 and 1e-7 (relative)
+    from their boundary (float32 logits tuned in float64): decided in float64
+    on the GPU, they equal the oracle's.  Float32 masses could not decide
+    them; float64 ones err by ~1e-16."""
+    from oracle.verify import _edge_margin, row_weights, uniforms
+    seed, V = 4242, 2 * 4096 + 77
+    Ls, ds, rids, poss = [], [], [], []
+    for j, delta in enumerate((3e-8, -3e-8, 1e-8, -1e-8)):
+        rid = np.array([1000 + 2 * j, 1001 + 2 * j])
+        pos = 50 + j
+        L, d = _band_rows(seed, rid, pos, V, delta)
+        # the crafted decisions really are that close (float64, as the oracle sees them)
+        u_acc, _ = uniforms(seed, int(rid[0]), pos + 1)
+        e = row_weights(L[0, 0], 1.0)
+        rel = e[5] / e.sum() / u_acc - 1.0
+        assert 1e-12 < abs(rel) < 2e-7 and np.sign(rel) == np.sign(delta), rel
+        _, u_res = uniforms(seed, int(rid[1]), pos + 2)
+        e = row_weights(L[1, 1], 1.0)
+        mg = _edge_margin(e, u_res * e.sum())
+        assert 1e-12 < mg < 2e-7, mg
+        Ls.append(L); ds.append(d); rids.append(rid); poss.append(np.full(2, pos))
+    L, d = np.concatenate(Ls), np.concatenate(ds)
+    rid, pos = np.concatenate(rids), np.concatenate(poss)
+    o, n = sample(dfl, dev, L, d, 1.0, seed, rid, pos)
+    o0, n0 = osamp(L, d, 1.0, seed, rid, pos)
+    assert np.array_equal(o, o0) and np.array_equal(n, n0)
+    # both outcomes of the acceptance test occur
+    assert set(n[0::2].tolist()) == {1, 2}, n
+
+
 def test_philox_bits_through_public_call(dfl, dev):
     """Equal logits, V = 2^23 + 1, draft = V - 1: a rejection emits exactly
     floor(u_res * 2^23) = w1 >> 41 of Philox4x64-10 for that request."""
