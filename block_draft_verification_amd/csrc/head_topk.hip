@@ -822,13 +822,23 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
 // (register-only inline asm, so the accumulators are never renamed or copied).
 //
 // W is read by one wavefront only, so it goes straight from memory into
-// registers in the MFMA operand layout: per chunk of 64 hidden columns, lane
-// (r, g) (r = lane % 16, g = lane / 16) loads bytes 16 g and 64 + 16 g of its
-// row's 128-byte line (k = 8 g and 32 + 8 g: the two k-steps), the two halves
-// back to back.  Chunk c+3 is requested as chunk c starts, so three chunks
-// are in flight beyond the one being multiplied: under a full streaming load
-// HBM answers in ~3.5 us, which takes ~100 KB in flight per CU (an LDS ring
-// that deep would not fit next to h).
+// registers.  Per 16-row tile and chunk of 64 hidden columns (one 128-byte
+// line per row) two loads cover whole lines: load A rows 0-7, load B rows
+// 8-15, lane (r, g) (r = lane % 16, g = lane / 16) taking 16-byte piece
+// g + 4 (r >= 8) of row r % 8 (or 8 + r % 8).  Whole lines per load cut the
+// requests the CU's memory pipeline must hold: with the two 64-byte halves
+// of every line in two loads (the plain operand layout, 16 rows x 64 bytes)
+// the loads stalled at issue for ~40 % of the loop at M = 224, and the loop
+// ran ~7 % longer.  (Eight consecutive lanes per line would let the
+// requests merge further, but the layout change back to the operand layout
+// then costs 14 VALU operations per dword pair, more than it saves.)  At the
+// chunk's start one row_ror:8 DPP move per dword (bank-masked to half of
+// each 16-lane row) turns A and B into the MFMA operand layout: lane (r, g)
+// then holds row r, piece g (k-step 0) and piece 4 + g (k-step 1).  Chunk
+// c+3 is requested as chunk c starts, so three chunks are in flight beyond
+// the one being multiplied: under a full streaming load HBM answers in
+// ~3.5 us, which takes ~100 KB in flight per CU (an LDS ring that deep would
+// not fit next to h).
 // h is shared by the four wavefronts: per chunk its 16*MT rows x 128 bytes go
 // straight into a 4-stage LDS ring with buffer_load_dwordx4 ... lds (no
 // register staging; rows unpadded, 16-byte pieces permuted piece ^ (row & 6),
@@ -898,7 +908,7 @@ __device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, co
         hdst[u] = j < C::HI ? j * 1024 : -1;
     }
 #pragma unroll
-    for (int t = 0; t < NTP; ++t) woff[t] = (16 * (wave + 4 * t) + ln) * D * 2 + lg * 16;
+    for (int t = 0; t < NTP; ++t) woff[t] = (16 * (wave + 4 * t) + (ln & 7)) * D * 2 + (lg + 4 * (ln >> 3)) * 16;
     // DMA: lane l writes bytes 16 l of its instruction's 1 KB (8 rows of 128
     // bytes): row l / 8, position l % 8, holding logical piece (l % 8) ^
     // ((l / 8) & 6); pieces past D (a ragged last chunk) load zeros
@@ -920,13 +930,32 @@ __device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, co
     u32x4 wq[4][NTP][2];  // W chunks in flight: slot c % 4
     auto issue_w = [&](u32x4 (&slot)[NTP][2], int c) __attribute__((always_inline)) {
         const int soff = c < nK ? c * 128 : 0;
+        const bool live = c < nK && c * C::KC + 8 * (lg + 4 * (ln >> 3)) < D;  // the piece lies within D
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const bool live = c < nK && c * C::KC + 32 * s + 8 * lg < D;
+        for (int s = 0; s < 2; ++s) {  // A: rows 0-7, B: rows 8-15 of the tile
 #pragma unroll
             for (int t = 0; t < NTP; ++t)
-                slot[t][s] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? woff[t] + 64 * s : kOffNone, soff, 0);
+                slot[t][s] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? woff[t] + s * 8 * D * 2 : kOffNone,
+                                                                   soff, 0);
         }
+    };
+    // A, B -> k-step 0, k-step 1 operands: lanes r >= 8 of each 16-lane row
+    // take B from lane r - 8 (k-step 0), lanes r < 8 take A from lane r + 8
+    // (k-step 1); the others keep what they loaded
+    auto arrange = [&](u32x4 (&slot)[NTP][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < NTP; ++t) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int a = (int)slot[t][0][j], b = (int)slot[t][1][j];
+                slot[t][0][j] = (uint32_t)__builtin_amdgcn_update_dpp(a, b, 0x128, 0xF, 0xC, false);
+                slot[t][1][j] = (uint32_t)__builtin_amdgcn_update_dpp(b, a, 0x128, 0xF, 0x3, false);
+            }
+        }
+        // the MFMAs (inline asm, invisible to the hazard checks) read these
+        // registers next: give the VALU writes their wait states
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 4" ::: "memory");
     };
     auto barrier = []() __attribute__((always_inline)) {
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -961,6 +990,8 @@ __device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, co
         // read their operands long before the data returns)
         __builtin_amdgcn_sched_barrier(0);
         issue_w(nslot, c + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        arrange(slot);  // (chunk c's loads have landed: h c, issued after them, was waited for)
         __builtin_amdgcn_sched_barrier(0);
         // k-step 0
 #pragma unroll
