@@ -36,6 +36,9 @@ _SIGNATURES = {
     "dflash_conv2tap_proj": (ctypes.c_int, [_p, _p, _p, _c_i64, _c_i32, _c_i32, _p]),
     "dflash_head_topk": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, _psz, _p]),
     "dflash_head_topk_noalloc": (ctypes.c_int, [_p, _p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p]),
+    "dflash_head_weight_bound": (ctypes.c_int, [_p, _c_i64, _c_i32, _p, _p]),
+    "dflash_head_topk_certify": (ctypes.c_int, [_p, _c_i64, _c_i32, _c_i64, _c_i32, _p, _p, _p, ctypes.c_size_t,
+                                                _p, _p]),
     "dflash_select_path": (ctypes.c_int, [_p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
                                           _p, _p, _p, _p, _psz, _p]),
     "dflash_select_path_anchored": (ctypes.c_int, [_p, _p, _p, _p, _p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32,
@@ -198,6 +201,42 @@ def head_topk(h, W, K=16, workspace=None, out=None):
     _check(L.dflash_head_topk(*before, _ptr(ws), ctypes.byref(nbytes), _stream(h.device)),
            "dflash_head_topk")
     return tv, ti
+
+
+def head_weight_bound(W):
+    """Bounds on W's rows for head_topk_certify: f32 [2] = (max row 2-norm,
+    max row 1-norm), rounded up."""
+    _need(W, torch.bfloat16, "W", 2)
+    V, D = W.shape
+    b = torch.empty(2, dtype=torch.float32, device=W.device)
+    _check(lib().dflash_head_weight_bound(_ptr(W), V, D, _ptr(b), _stream(W.device)), "dflash_head_weight_bound")
+    return b
+
+
+def head_topk_certified(h, W, bound, K=16):
+    """head_topk and its exactness certificate: (top_val, top_idx, certified
+    i32 [M]: 1 where the 16 are shown to be the exact top-16).  bound from
+    head_weight_bound(W)."""
+    _need(h, torch.bfloat16, "h", 2)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(bound, torch.float32, "bound", 1)
+    if bound.numel() != 2:
+        raise DFlashError("bound must hold 2 floats (head_weight_bound)")
+    M, D = h.shape
+    V = W.shape[0]
+    if W.shape[1] != D:
+        raise DFlashError("W must be [V][D] with the same D as h")
+    _same_device("head_topk_certified", h, W, bound)
+    L = lib()
+    tv = torch.empty((M, K), dtype=torch.float32, device=h.device)
+    ti = torch.empty((M, K), dtype=torch.int32, device=h.device)
+    before = (_ptr(h), _ptr(W), M, D, V, K, _ptr(tv), _ptr(ti))
+    ws, nbytes = _workspace(L.dflash_head_topk, before, (_stream(h.device),), h.device, None)
+    _check(L.dflash_head_topk(*before, _ptr(ws), ctypes.byref(nbytes), _stream(h.device)), "dflash_head_topk")
+    cert = torch.empty(M, dtype=torch.int32, device=h.device)
+    _check(L.dflash_head_topk_certify(_ptr(h), M, D, V, K, _ptr(bound), _ptr(tv), _ptr(ws), nbytes.value,
+                                      _ptr(cert), _stream(h.device)), "dflash_head_topk_certify")
+    return tv, ti, cert
 
 
 def head_topk_noalloc(h, W, K=16, out=None):

@@ -19,6 +19,9 @@ size_t head_workspace_bytes(int64_t M, int64_t V);
 size_t head_static_scratch_bytes();
 int launch_head_topk_static(const uint16_t*, const uint16_t*, int64_t, int, int64_t, float*, int32_t*,
                             hipStream_t);
+int launch_head_weight_bound(const uint16_t*, int64_t, int, float*, hipStream_t);
+int launch_head_certify(const uint16_t*, int64_t, int, int64_t, const float*, const float*, const void*, int32_t*,
+                        hipStream_t);
 int launch_select_path(const float*, const int32_t*, const int32_t*, const float*, const float*, int, int, int64_t,
                        int, int32_t*, int32_t*, float*, void*, hipStream_t);
 size_t select_workspace_bytes(int B, int P, bool anchored);
@@ -169,6 +172,34 @@ int dflash_head_topk_noalloc(const uint16_t* h, const uint16_t* W, int64_t M, in
     st = check_device();
     if (st != DFLASH_OK) return st;
     return launch_head_topk_static(h, W, M, D, V, top_val, top_idx, (hipStream_t)stream);
+}
+
+int dflash_head_weight_bound(const uint16_t* W, int64_t V, int32_t D, float* bound, void* stream) {
+    if (!W || !bound) return DFLASH_ERR_INVALID;
+    if (D < 8 || D % 8 != 0 || D > 65536 || V < 1 || V >= ((int64_t)1 << 31)) return DFLASH_ERR_INVALID;
+    if (!aligned16(W) || !aligned4(bound) || overlap(bound, 8, W, (size_t)V * D * 2)) return DFLASH_ERR_INVALID;
+    const int st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_head_weight_bound(W, V, D, bound, (hipStream_t)stream);
+}
+
+int dflash_head_topk_certify(const uint16_t* h, int64_t M, int32_t D, int64_t V, int32_t K, const float* bound,
+                             const float* top_val, const void* workspace, size_t workspace_bytes,
+                             int32_t* certified, void* stream) {
+    if (!h || !bound || !top_val || !workspace || !certified) return DFLASH_ERR_INVALID;
+    if (M < 1 || D < 8 || D % 8 != 0 || D > 65536 || V < 1) return DFLASH_ERR_INVALID;
+    if (K != 16) return DFLASH_ERR_UNSUPPORTED;
+    if (V < K || V >= ((int64_t)1 << 31) || M > ((int64_t)1 << 24)) return DFLASH_ERR_INVALID;
+    if (!aligned16(h) || !aligned4(bound) || !aligned4(top_val) || !aligned16(workspace) || !aligned4(certified))
+        return DFLASH_ERR_INVALID;
+    if (workspace_bytes < head_workspace_bytes(M, V)) return DFLASH_ERR_WORKSPACE;
+    const size_t nc = (size_t)M * 4;
+    if (overlap(certified, nc, h, (size_t)M * D * 2) || overlap(certified, nc, top_val, (size_t)M * K * 4) ||
+        overlap(certified, nc, workspace, workspace_bytes) || overlap(certified, nc, bound, 8))
+        return DFLASH_ERR_INVALID;
+    const int st = check_device();
+    if (st != DFLASH_OK) return st;
+    return launch_head_certify(h, M, D, V, bound, top_val, workspace, certified, (hipStream_t)stream);
 }
 
 // Draws of the sampled-path selector (on = false: the max-sum selector).

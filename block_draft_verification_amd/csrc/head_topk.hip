@@ -1869,4 +1869,156 @@ int launch_head_stats(const uint16_t* h, const uint16_t* W, int64_t M, int D, in
     return launch_status();
 }
 
+// ------------------------------------------------ exactness certificate
+// The head returns the best 16 of its best kRescore float32 candidates by
+// exact value.  An entry outside those candidates could still belong in the
+// exact top-16 if its float32 logit erred by more than the gap.  For row m:
+//  * every float32 logit f_v (the GEMM's float32 accumulation of D exact
+//    bf16 products) satisfies |f_v - z_v| <= eps_m = gamma_D min(|h_m|_2 N2,
+//    |h_m|_inf N1), with N2, N1 bounds on max_v |W_v|_2 and max_v |W_v|_1 and
+//    gamma_D = D u / (1 - D u), u = 2^-23: one unit in the last place per
+//    addition, whatever the order and the direction of rounding;
+//  * U = the largest float32 value among entries that were not re-scored:
+//    the best list head left once the re-scored keys are taken from the
+//    partial lists, or the 16th entry of a list all of whose entries were
+//    taken (its unseen entries are no larger);
+//  * L16 = a lower bound of the exact 16th value (its float32 rounding minus
+//    half a unit in the last place).
+// L16 > U + eps_m means every entry outside the candidates has z_v < z_16:
+// the 16 returned are the exact top-16.
+
+// N2 and N1 (rounded up) over W's rows; out must be zeroed first.
+__global__ __launch_bounds__(256) void head_weight_bound_kernel(const uint16_t* __restrict__ W, int64_t V, int D,
+                                                                unsigned* __restrict__ out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    double best2 = 0.0, best1 = 0.0;
+    for (int64_t v = (int64_t)blockIdx.x * 4 + wave; v < V; v += (int64_t)gridDim.x * 4) {
+        const uint16_t* wr = W + v * D;
+        double s2 = 0.0, s1 = 0.0;
+        for (int k = lane * 8; k < D; k += 512) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(wr + k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const double a = bf16_to_f32(q[j] & 0xFFFFu), b = bf16_to_f32(q[j] >> 16);
+                s2 = fma(a, a, fma(b, b, s2));
+                s1 += fabs(a) + fabs(b);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            s2 += __shfl_xor(s2, off);
+            s1 += __shfl_xor(s1, off);
+        }
+        best2 = fmax(best2, s2);
+        best1 = fmax(best1, s1);
+    }
+    if (lane == 0) {
+        // float64 sums of at most 65536 terms err by less than 2^-37 relative
+        const float n2 = __double2float_ru(sqrt(best2) * (1.0 + 0x1p-30));
+        const float n1 = __double2float_ru(best1 * (1.0 + 0x1p-30));
+        atomicMax(out + 0, __float_as_uint(n2));  // non-negative floats order as their bits
+        atomicMax(out + 1, __float_as_uint(n1));
+    }
+}
+
+__global__ void head_bound_clear_kernel(unsigned* out) {
+    if (threadIdx.x < 2) out[threadIdx.x] = 0u;
+}
+
+// One wavefront per row: the exact-top-16 certificate from the partial lists
+// the head left in its workspace (pv, pi: [M][S][16], sorted per list).
+__global__ __launch_bounds__(64) void head_certify_kernel(const uint16_t* __restrict__ h, int D, int S,
+                                                          const float* __restrict__ pv, const int* __restrict__ pi,
+                                                          const float* __restrict__ top_val,
+                                                          const float* __restrict__ bound,
+                                                          int32_t* __restrict__ certified) {
+    const int64_t m = blockIdx.x;
+    const int lane = threadIdx.x;
+    const uint16_t* hr = h + m * D;
+    double s2 = 0.0, mx = 0.0;
+    for (int k = lane; k < D; k += 64) {
+        const double x = bf16_to_f32(hr[k]);
+        s2 = fma(x, x, s2);
+        mx = fmax(mx, fabs(x));
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        s2 += __shfl_xor(s2, off);
+        mx = fmax(mx, __shfl_xor(mx, off));
+    }
+    // k-way extraction over the lists: lane l holds the heads of lists
+    // l, l + 64, ...; 0 marks no list (below every key)
+    constexpr int kPer = kMaxLists / 64;
+    const float* rv = pv + m * S * kTopK;
+    const int* ri = pi + m * S * kTopK;
+    int ptr[kPer];
+    uint64_t head[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int l = lane + 64 * j;
+        ptr[j] = 0;
+        head[j] = l < S ? rank_key(rv[l * kTopK], ri[l * kTopK]) : 0ull;
+    }
+    float exhausted = -INFINITY;  // 16th value of lists taken whole
+    uint64_t next = 0ull;         // the best key left after the candidates
+    for (int it = 0; it <= kRescore; ++it) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) best = head[j] > best ? head[j] : best;
+        uint64_t w = best;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t o = shfl_xor_u64(w, off);
+            w = o > w ? o : w;
+        }
+        if (it == kRescore || w <= kEmptyKey) {  // past the candidates, or only empty entries left
+            next = w;
+            break;
+        }
+        if (best == w) {  // the list holding it (ids are unique) moves on
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                if (head[j] == w) {
+                    const int l = lane + 64 * j;
+                    if (++ptr[j] < kTopK) {
+                        head[j] = rank_key(rv[l * kTopK + ptr[j]], ri[l * kTopK + ptr[j]]);
+                    } else {
+                        exhausted = fmaxf(exhausted, rv[l * kTopK + kTopK - 1]);
+                        head[j] = 0ull;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) exhausted = fmaxf(exhausted, __shfl_xor(exhausted, off));
+    const double U = fmax((double)(next > kEmptyKey ? key_value(next) : -INFINITY), (double)exhausted);
+    const double u = 0x1p-23, Du = (double)D * u;
+    const double gamma = Du / (1.0 - Du);
+    const double eps = gamma * fmin(sqrt(s2) * (double)bound[0], mx * (double)bound[1]) * (1.0 + 0x1p-30);
+    const double tv = (double)top_val[m * kTopK + kTopK - 1];
+    const double L16 = tv - fabs(tv) * 0x1p-24 - 0x1p-149;
+    if (lane == 0) certified[m] = L16 > U + eps ? 1 : 0;
+}
+
+int launch_head_weight_bound(const uint16_t* W, int64_t V, int D, float* bound, hipStream_t stream) {
+    unsigned* out = reinterpret_cast<unsigned*>(bound);
+    hipLaunchKernelGGL(head_bound_clear_kernel, dim3(1), dim3(64), 0, stream, out);
+    int st = launch_status();
+    if (st != DFLASH_OK) return st;
+    const int64_t blocks = std::min<int64_t>((V + 3) / 4, 8 * kCUs);
+    hipLaunchKernelGGL(head_weight_bound_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, V, D, out);
+    return launch_status();
+}
+
+int launch_head_certify(const uint16_t* h, int64_t M, int D, int64_t V, const float* bound, const float* top_val,
+                        const void* ws, int32_t* certified, hipStream_t stream) {
+    const HeadPlan p = head_plan(M, V);
+    const float* pv = reinterpret_cast<const float*>(ws);
+    const int* pi = reinterpret_cast<const int*>(pv + (size_t)M * p.S * kTopK);
+    hipLaunchKernelGGL(head_certify_kernel, dim3((unsigned)M), dim3(64), 0, stream, h, D, p.S, pv, pi, top_val,
+                       bound, certified);
+    return launch_status();
+}
+
 }  // namespace dflash

@@ -166,6 +166,47 @@ int dflash_head_topk_noalloc(const uint16_t* h, const uint16_t* W, int64_t M,
                              int32_t* top_idx, void* stream);
 
 /*
+ * Bounds on the rows of an LM head W, for dflash_head_topk_certify: bound[0]
+ * >= max_v |W_v|_2 and bound[1] >= max_v |W_v|_1 (sums in float64, rounded
+ * up to float32).  One pass over W; compute it once per weight matrix.
+ *   W      bf16 [V][D] (16-byte aligned)
+ *   bound  f32 [2] device, written on `stream`
+ * Requires D % 8 == 0, 8 <= D <= 65536, 1 <= V < 2^31.
+ */
+int dflash_head_weight_bound(const uint16_t* W, int64_t V, int32_t D, float* bound,
+                             void* stream);
+
+/*
+ * Certificate that dflash_head_topk's results are the exact top-16.
+ * Source: the exactness contract of the head (top-k over exact logits, see
+ * dflash_head_topk).  The head ranks its best 20 float32 candidates by their
+ * exact values; an entry it did not re-score can only displace one of the 16
+ * returned if its float32 logit erred by more than the gap.  Per row m:
+ * certified[m] = 1 iff L16 > U + eps_m, where L16 is a lower bound of the
+ * exact 16th value (top_val[m][15] minus half an ulp), U the largest float32
+ * value among entries that were not re-scored (read from the partial lists
+ * the head left in its workspace), and eps_m = gamma_D * min(|h_m|_2 *
+ * bound[0], |h_m|_inf * bound[1]) with gamma_D = D u / (1 - D u), u = 2^-23
+ * (an error of one unit in the last place per float32 addition, in any order
+ * and rounding direction).  certified[m] = 0 does not mean the row is wrong,
+ * only that this bound cannot show it; the caller may recompute such rows
+ * (e.g. with the exact logits of their candidates).
+ *   h          bf16 [M][D]      as given to dflash_head_topk
+ *   bound      f32 [2]          from dflash_head_weight_bound on the same W
+ *   top_val    f32 [M][16]      dflash_head_topk's output
+ *   workspace  the workspace of that dflash_head_topk call (its partial
+ *              lists), unchanged since; workspace_bytes its size
+ *   certified  i32 [M]          1 certified exact, 0 not shown
+ * Enqueue it on the same stream after dflash_head_topk.  Requires the same
+ * M, D, V, K as that call; a smaller workspace than it needs returns
+ * DFLASH_ERR_WORKSPACE.
+ */
+int dflash_head_topk_certify(const uint16_t* h, int64_t M, int32_t D, int64_t V, int32_t K,
+                             const float* bound, const float* top_val,
+                             const void* workspace, size_t workspace_bytes,
+                             int32_t* certified, void* stream);
+
+/*
  * Pair selector: one coherent path through the P x K candidate lattice.
  * Source: tamsi.dev, section "L'idee, sans le papier" (a pair selector of
  * about 2 M parameters chooses a coherent path among good candidates);

@@ -269,3 +269,23 @@ def test_sample_fused_validation():
     assert call(tau=0.0) == INVALID and call(tau=float("nan")) == INVALID and call(rid=None) == INVALID
     assert call(T=17) == INVALID and call(V=8) == INVALID and call(D=12) == INVALID
     assert call(out=P8[2]) == INVALID
+
+
+@needs_lib
+def test_certify_and_bound_validation():
+    L = dfl.lib()
+    S0 = ctypes.c_void_p(0)
+    # weight bound: null pointers, bad D, GPU-less host
+    assert L.dflash_head_weight_bound(NULL, 100, 64, A[1], NULL) == INVALID
+    assert L.dflash_head_weight_bound(A[0], 100, 60, A[1], NULL) == INVALID
+    assert L.dflash_head_weight_bound(A[0], 0, 64, A[1], NULL) == INVALID
+    assert L.dflash_head_weight_bound(A[0], 100, 64, A[1], NULL) in (DEVICE, OK)
+    # certify: K, sizes, a workspace smaller than the head's
+    need = ctypes.c_size_t(0)
+    assert L.dflash_head_topk(A[0], A[1], 224, 256, 8192, 16, A[2], A[3], NULL, ctypes.byref(need), NULL) == OK
+    args = lambda K=16, ws=need.value, M=224: (A[0], M, 256, 8192, K, A[4], A[2], A[5], ws, A[6], NULL)
+    assert L.dflash_head_topk_certify(*args(K=8)) == UNSUPPORTED
+    assert L.dflash_head_topk_certify(*args(M=0)) == INVALID
+    assert L.dflash_head_topk_certify(*args(ws=need.value - 16)) == WORKSPACE
+    assert L.dflash_head_topk_certify(A[0], 224, 256, 8192, 16, NULL, A[2], A[5], need.value, A[6], NULL) == INVALID
+    assert L.dflash_head_topk_certify(*args()) in (DEVICE, OK)
