@@ -80,6 +80,10 @@ def parse():
     ap.add_argument("--copy-probe", type=float, default=None, metavar="GIB",
                     help="only copy a GIB-sized device buffer 3 times (calibrates rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only time, at each workload's head shape, the vendor GEMM of the logits "
+                         "(torch.mm, bf16 inputs, bf16 and fp32 outputs, no top-k) beside "
+                         "dflash_head_topk (GEMM and top-16), and exit")
     return ap.parse_args()
 
 
@@ -93,6 +97,50 @@ def copy_probe(gib):
         b.copy_(a)
     torch.cuda.synchronize()
     log(f"[bench] copy probe: 3 copies of {n} bytes")
+
+
+def gemm_probe():
+    """The head's GEMM at each workload's shape through the vendor library
+    (torch.mm on ROCm: hipBLASLt), which materialises the logits and keeps no
+    top-k, timed beside dflash_head_topk on the same operands: a reference for
+    what the bf16 GEMM of this shape reaches on the chip."""
+    import torch
+    import block_draft_verification_amd as dfl
+    from workload.configs import get_config
+    dev = torch.device("cuda:0")
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1000.0 / reps
+
+    W_by_v = {}
+    for name in ("c2_b1", "c3_b8", "c4_b32", "c5_stress"):
+        cfg = get_config(name)
+        M, V, D = cfg.M, cfg.V, cfg.D
+        if V not in W_by_v:
+            W_by_v.clear()
+            g = torch.Generator(device=dev).manual_seed(1)
+            W_by_v[V] = (0.02 * torch.randn(V, D, device=dev, generator=g)).to(torch.bfloat16)
+        W = W_by_v[V]
+        g = torch.Generator(device=dev).manual_seed(2)
+        h = torch.randn(M, D, device=dev, generator=g).to(torch.bfloat16)
+        flops = 2.0 * M * V * D
+        rec = {"probe": "head GEMM", "workload": name, "M": M, "V": V, "D": D,
+               "torch_mm_bf16_out_us": round(timed(lambda: torch.mm(h, W.t())), 1),
+               "torch_mm_fp32_out_us": round(timed(lambda: torch.mm(h, W.t(), out_dtype=torch.float32)), 1),
+               "dflash_head_topk_us": round(timed(lambda: dfl.head_topk(h, W)), 1)}
+        for k in ("torch_mm_bf16_out_us", "torch_mm_fp32_out_us", "dflash_head_topk_us"):
+            rec[k.replace("_us", "_tflops")] = round(flops / rec[k] / 1e6, 1)
+        print(json.dumps(rec), flush=True)
 
 
 class CycleRunner:
@@ -424,6 +472,9 @@ def main():
     args = parse()
     if args.copy_probe is not None:
         copy_probe(args.copy_probe)
+        return
+    if args.gemm_probe:
+        gemm_probe()
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -852,6 +852,10 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
 //
 // After each strip the running top-16 lists (in LDS for the whole call)
 // absorb the strip's logits (strip_topk).
+// floats per lane in the epilogue's value rows (16 values; rows 16-byte
+// aligned and spread over the LDS banks)
+constexpr int kValsPitch = 20;
+
 template <int MT, int NT>
 struct MfmaCfg {
     static constexpr int MB = 16 * MT;            // rows of h per workgroup
@@ -875,8 +879,8 @@ struct MfmaCfg {
     static constexpr size_t LISTS = SPARE + 1024;           // lists, thresholds, slot counters
     static constexpr size_t LDS = LISTS + (size_t)MB * (kTopK * 8 + 8);
     static constexpr int CAP = 32;                // candidate keys per row and round
-    static_assert((size_t)MB * CAP * 8 <= SPARE && (size_t)MB * 64 * 4 <= SPARE,
-                  "candidates and seed lists fit in the drained ring");
+    static_assert((size_t)MB * CAP * 8 + 256 * kValsPitch * 4 <= SPARE && (size_t)MB * 64 * 4 <= SPARE,
+                  "candidates, value rows and seed lists fit in the drained ring");
     static_assert(LDS <= 160 * 1024, "LDS per workgroup");
     static_assert(MT * NT * 4 <= 240 && NT <= 8, "accumulators fit in the AGPRs");
     static_assert(PF <= MT && (2 * MT) % R == 0, "prefetch distance within a k-step");
@@ -1046,6 +1050,7 @@ struct StripLists {
     int* cnt;         // [MB] candidate slots reserved this round (may pass CAP)
     uint64_t* cand;   // [MB][CAP] candidate keys (the drained ring)
     float* seed;      // [MB][4][16] per-wavefront sorted lane maxima (first strip; aliases cand)
+    float* vals;      // [256][kValsPitch] each lane's values of one fragment row (after cand)
 };
 
 // One strip's logits, still in the accumulators, into the running lists.
@@ -1069,6 +1074,7 @@ template <int MT, int NT>
 __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const StripLists& sl, int wave, int lane_in,
                                            int rows_blk, int64_t col0, int nt_act, int64_t V, bool first) {
     constexpr int CAP = MfmaCfg<MT, NT>::CAP;
+    static_assert(4 * NT <= kValsPitch, "a fragment row's values fit in the lane's value row");
     int lane = lane_in;
     asm volatile("" : "+v"(lane));
     const int ln = lane & 15, lg = lane >> 4;
@@ -1091,6 +1097,7 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
     auto* list_g = base(sl.list + g * kTopK + ln);
     auto* cnt_g = base(sl.cnt + g);
     auto* thr_g = base(sl.thr + g);
+    auto* vals_l = base(sl.vals + (wave * 64 + lane) * kValsPitch);
     // accumulators are read where they are used, straight from their AGPRs:
     // copies kept in VGPRs across the rounds would not fit
     auto rd = [](const float& x) __attribute__((always_inline)) {
@@ -1169,8 +1176,7 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
                     if (rd(acc[i][t][q]) >= tq[q]) m |= 1u << (4 * t + q);
-            m &= pend[i];
-            pend[i] = m;  // below the threshold: never again
+            m &= pend[i];  // below the threshold: never again
             // one reservation per lane and row (row 16 i + 4 lg + q): a run of
             // slots as long as the lane's candidates for that row; the four
             // reservations are issued back to back
@@ -1180,19 +1186,37 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
                 const int n = __builtin_popcount(m & (0x1111u << q));
                 base[q] = n ? atomicAdd(cnt_at(i, q), n) : CAP;
             }
+            // the four bases in 16-bit fields (a row takes at most 256
+            // reservations per round), selected by a shift below
+            uint64_t bases = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int slot = base[q];
+            for (int q = 0; q < 4; ++q) bases |= (uint64_t)(uint32_t)base[q] << (16 * q);
+            // The lane's 16 values go to its LDS scratch row, and the stores
+            // visit only the set bits of m (a value is then read back by its
+            // bit index; indexing the accumulators by it would go through
+            // scratch memory).  A candidate's slot is its row's base plus
+            // the lane's candidates of that row at lower bits; those past
+            // the buffer stay pending.
 #pragma unroll
-                for (int t = 0; t < NT; ++t) {
-                    const uint32_t bit = 1u << (4 * t + q);
-                    if ((m & bit) && slot < CAP) {
-                        cand_at(i, q)[slot] = rank_key(rd(acc[i][t][q]), (int)(col0 + 16 * (wave + 4 * t) + ln));
-                        pend[i] &= ~bit;  // offered; a candidate past the buffer stays pending
-                    }
-                    slot += (m & bit) ? 1 : 0;
+            for (int t = 0; t < NT; ++t) {
+                floatx4 v4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v4[q] = rd(acc[i][t][q]);
+                *(__attribute__((address_space(3))) floatx4*)(vals_l + 4 * t) = v4;
+            }
+            uint32_t todo = m, left = m;
+            while (todo) {
+                const int b = __builtin_ctz(todo);
+                todo &= todo - 1;
+                const int q = b & 3;
+                const int slot = (int)((bases >> (16 * q)) & 0xFFFFu) +
+                                 __builtin_popcount(m & (0x1111u << q) & ((1u << b) - 1u));
+                if (slot < CAP) {
+                    cand_at(i, q)[slot] = rank_key(vals_l[b], (int)(col0 + 16 * (wave + 4 * (b >> 2)) + ln));
+                    left &= ~(1u << b);
                 }
             }
+            pend[i] = left;
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
@@ -1257,6 +1281,7 @@ void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, in
     sl.cnt = reinterpret_cast<int*>(sl.thr + C::MB);
     sl.cand = reinterpret_cast<uint64_t*>(smem);  // the drained ring (epilogue only)
     sl.seed = reinterpret_cast<float*>(smem);
+    sl.vals = reinterpret_cast<float*>(smem + (size_t)C::MB * C::CAP * 8);
     for (int e = tid; e < C::MB * kTopK; e += 256) sl.list[e] = kEmptyKey;
     for (int e = tid; e < C::MB; e += 256) {
         sl.thr[e] = -INFINITY;
