@@ -1220,26 +1220,46 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
             __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
-        // 16-lane group g merges rows g, g + 16, ...: those with candidates
+        // 16-lane group g merges rows g, g + 16, ... that received
+        // candidates, two rows at a time so that their sorting networks
+        // interleave (with one wavefront per SIMD, a single network's
+        // dependent steps would each wait out the full latency); the partner
+        // of a row with candidates may merge only empty keys, which leave its
+        // list as it is, and is not written back.
         int nrow[MT];
 #pragma unroll
         for (int j = 0; j < MT; ++j) nrow[j] = cnt_g[16 * j];
 #pragma unroll
-        for (int j = 0; j < MT; ++j) {
-            const int n = min(nrow[j], CAP);
-            if (n == 0) continue;
-            auto* lst = list_g + 16 * kTopK * j;
-            const auto* cnd = cand_g + 16 * CAP * j;
-            uint64_t lk = *lst;
+        for (int j = 0; j < MT; j += 2) {
+            const bool two = j + 1 < MT;
+            const int n0 = min(nrow[j], CAP), n1 = two ? min(nrow[j + 1], CAP) : 0;
+            if (n0 == 0 && n1 == 0) continue;
+            auto* lst0 = list_g + 16 * kTopK * j;
+            auto* lst1 = list_g + 16 * kTopK * (two ? j + 1 : j);
+            const auto* cnd0 = cand_g + 16 * CAP * j;
+            const auto* cnd1 = cand_g + 16 * CAP * (two ? j + 1 : j);
+            uint64_t l0 = *lst0, l1 = *lst1;
+            const int n = max(n0, n1);
             for (int c0 = 0; c0 < n; c0 += 16) {
-                uint64_t ck = c0 + ln < n ? cnd[c0] : kEmptyKey;
-                ck = sort16<false>(ck, ln);
-                lk = lk > ck ? lk : ck;
-                lk = merge16_desc(lk, ln);
+                uint64_t k0 = c0 + ln < n0 ? cnd0[c0] : kEmptyKey;
+                uint64_t k1 = c0 + ln < n1 ? cnd1[c0] : kEmptyKey;
+                k0 = sort16<false>(k0, ln);
+                k1 = sort16<false>(k1, ln);
+                l0 = l0 > k0 ? l0 : k0;
+                l1 = l1 > k1 ? l1 : k1;
+                l0 = merge16_desc(l0, ln);
+                l1 = merge16_desc(l1, ln);
             }
-            *lst = lk;
-            if (ln == kTopK - 1) thr_g[16 * j] = key_value(lk);
-            if (ln == 0) cnt_g[16 * j] = 0;
+            if (n0 > 0) {
+                *lst0 = l0;
+                if (ln == kTopK - 1) thr_g[16 * j] = key_value(l0);
+                if (ln == 0) cnt_g[16 * j] = 0;
+            }
+            if (n1 > 0) {
+                *lst1 = l1;
+                if (ln == kTopK - 1) thr_g[16 * (j + 1)] = key_value(l1);
+                if (ln == 0) cnt_g[16 * (j + 1)] = 0;
+            }
         }
         int any = 0;
 #pragma unroll
