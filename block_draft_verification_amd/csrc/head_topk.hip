@@ -892,7 +892,7 @@ struct MfmaCfg {
 // One strip's K loop.  NTP <= NT: only the wavefront's first NTP column tiles
 // are multiplied (a partial last strip; the others keep zeros and are not
 // admitted); rows past M are multiplied as zeros and never admitted either.
-template <int MT, int NT, int NTP>
+template <int MT, int NT, int NTP, int WAUX>
 __device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, const __amdgpu_buffer_rsrc_t wsrc,
                                            int D, int nK, int wave, int lane_in, floatx4 (&acc)[MT][NT]) {
     using C = MfmaCfg<MT, NT>;
@@ -940,7 +940,7 @@ __device__ __forceinline__ void mfma_strip(const __amdgpu_buffer_rsrc_t hsrc, co
 #pragma unroll
             for (int t = 0; t < NTP; ++t)
                 slot[t][s] = __builtin_amdgcn_raw_buffer_load_b128(wsrc, live ? woff[t] + s * 8 * D * 2 : kOffNone,
-                                                                   soff, 0);
+                                                                   soff, WAUX);
         }
     };
     // A, B -> k-step 0, k-step 1 operands: lanes r >= 8 of each 16-lane row
@@ -1268,7 +1268,7 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
     }
 }
 
-template <int MT, int NT>
+template <int MT, int NT, int WAUX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, int64_t n_tiles, int S,
                       int n_mb, float* __restrict__ part_val, int* __restrict__ part_idx) {
@@ -1325,11 +1325,11 @@ void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, in
         // multiplies only as many column tiles as the busiest wavefront holds
         const int need = (tiles_here + 3) / 4;
         if (need > NT / 2)
-            mfma_strip<MT, NT, NT>(hsrc, wsrc, D, nK, wave, lane, acc);
+            mfma_strip<MT, NT, NT, WAUX>(hsrc, wsrc, D, nK, wave, lane, acc);
         else if (need > 1)
-            mfma_strip<MT, NT, NT / 2>(hsrc, wsrc, D, nK, wave, lane, acc);
+            mfma_strip<MT, NT, NT / 2, WAUX>(hsrc, wsrc, D, nK, wave, lane, acc);
         else
-            mfma_strip<MT, NT, 1>(hsrc, wsrc, D, nK, wave, lane, acc);
+            mfma_strip<MT, NT, 1, WAUX>(hsrc, wsrc, D, nK, wave, lane, acc);
         strip_topk<MT, NT>(acc, sl, wave, lane, rows_blk, col0, nt_act, V, t0 == t_begin);
         __syncthreads();  // the ring (epilogue scratch) is refilled by the next strip
     }
@@ -1666,18 +1666,28 @@ struct WideVariant {
 };
 
 // One instantiation of head_mfma_kernel with its launch.
+// W's loads are non-temporal when each W row is read by one workgroup (one
+// M-block; measured 3-4 % faster at M = 128 and 224), and cached when the
+// M-blocks of a slot share W rows through L2 (non-temporal there measured
+// 1.5 % slower at M = 480).
 template <int MT, int NT>
 struct MfmaVariant {
     using Cfg = MfmaCfg<MT, NT>;
-    static const void* fn() { return reinterpret_cast<const void*>(&head_mfma_kernel<MT, NT>); }
+    template <int WAUX>
+    static const void* fn() { return reinterpret_cast<const void*>(&head_mfma_kernel<MT, NT, WAUX>); }
     static void set_attr() {
-        (void)hipFuncSetAttribute(fn(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+        (void)hipFuncSetAttribute(fn<0>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
+        (void)hipFuncSetAttribute(fn<kBufNT>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
     }
     static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
                        int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
         const int grid = (S + 7) / 8 * 8 * n_mb;
-        hipLaunchKernelGGL((head_mfma_kernel<MT, NT>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M, D, V,
-                           n_tiles, S, n_mb, pv, pi);
+        if (n_mb == 1)
+            hipLaunchKernelGGL((head_mfma_kernel<MT, NT, kBufNT>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M,
+                               D, V, n_tiles, S, n_mb, pv, pi);
+        else
+            hipLaunchKernelGGL((head_mfma_kernel<MT, NT, 0>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M, D, V,
+                               n_tiles, S, n_mb, pv, pi);
     }
 };
 using Mfma128 = MfmaVariant<8, 4>;   // M-blocks of 128 rows, 256-row strips
