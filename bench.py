@@ -82,8 +82,8 @@ def parse():
                          "FETCH_SIZE / WRITE_SIZE against known bytes) and exit")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only time, at each workload's head shape, the vendor GEMM of the logits "
-                         "(torch.mm, bf16 inputs, bf16 and fp32 outputs, no top-k) beside "
-                         "dflash_head_topk (GEMM and top-16), and exit")
+                         "(torch.mm, bf16 inputs, bf16 and fp32 outputs, no top-k) and a torch.topk "
+                         "over its fp32 logits, beside dflash_head_topk (GEMM and top-16), and exit")
     return ap.parse_args()
 
 
@@ -138,6 +138,9 @@ def gemm_probe():
                "torch_mm_bf16_out_us": round(timed(lambda: torch.mm(h, W.t())), 1),
                "torch_mm_fp32_out_us": round(timed(lambda: torch.mm(h, W.t(), out_dtype=torch.float32)), 1),
                "dflash_head_topk_us": round(timed(lambda: dfl.head_topk(h, W)), 1)}
+        z = torch.mm(h, W.t(), out_dtype=torch.float32)
+        rec["torch_topk16_of_fp32_logits_us"] = round(timed(lambda: torch.topk(z, 16, dim=1)), 1)
+        del z
         for k in ("torch_mm_bf16_out_us", "torch_mm_fp32_out_us", "dflash_head_topk_us"):
             rec[k.replace("_us", "_tflops")] = round(flops / rec[k] / 1e6, 1)
         print(json.dumps(rec), flush=True)
