@@ -1,9 +1,11 @@
 """HIP-graph capture of a whole cycle through the C-ABI.
 
 Every call only enqueues kernels on the caller's stream (no allocation, no
-memset, no synchronisation), so a cycle can be captured once and replayed.
-Each replay, with eager work and synchronisations in between, must give
-exactly the outputs of the eager cycle.
+memset, no synchronisation), so a cycle can be captured once and replayed,
+also with the greedy and sampled halves of a batch verified on two streams
+(as the benchmark's graph does).  Each replay, with eager work and
+synchronisations in between, must give exactly the outputs of the eager
+cycle.
 """
 
 import numpy as np
@@ -15,9 +17,12 @@ from workload import get_config, make_cycle_inputs
 pytestmark = pytest.mark.gpu
 
 
-def _cycle(dfl, g, cfg, bufs, bound, fused=False):
+def _cycle(dfl, g, cfg, bufs, bound, fused=False, side=None):
     """fused: the conv projects its own taps, and verification runs from the
-    target's hidden states through the LM head."""
+    target's hidden states through the LM head.  side: a second stream on
+    which the greedy half verifies, forked after the selector and joined at
+    the end (the two halves touch disjoint requests, outputs and
+    workspaces)."""
     B, P, T = cfg.B, cfg.P, cfg.T
     calls = []
     for l in range(cfg.L):
@@ -29,19 +34,34 @@ def _cycle(dfl, g, cfg, bufs, bound, fused=False):
     calls.append(bound.bind_select_path(bufs["tv"].view(B, P, 16), bufs["ti"].view(B, P, 16), g["F_l"], g["F_r"],
                                         bufs["rank"], bufs["tok"], bufs["score"], bufs["ws_s"]))
     h = B // 2
-    if fused:
-        calls.append(bound.bind_verify_greedy_fused(g["h_target"][:h * T], g["W"], bufs["tok"][:h], bufs["out"][:h],
-                                                    bufs["n"][:h], bufs["ws_g"]))
-        calls.append(bound.bind_verify_sample_fused(g["h_target"][h * T:], g["W"], bufs["tok"][h:], 1.0, 7,
-                                                    g["request_id"][h:], g["pos0"][h:], bufs["out"][h:],
-                                                    bufs["n"][h:], bufs["ws_v"]))
-    else:
-        calls.append(bound.bind_verify_greedy(g["target"][:h], bufs["tok"][:h], bufs["out"][:h], bufs["n"][:h],
-                                              bufs["ws_g"]))
-        calls.append(bound.bind_verify_sample(g["target"][h:], bufs["tok"][h:], 1.0, 7, g["request_id"][h:],
-                                              g["pos0"][h:], bufs["out"][h:], bufs["n"][h:], bufs["ws_v"]))
+
+    def greedy():
+        if fused:
+            return bound.bind_verify_greedy_fused(g["h_target"][:h * T], g["W"], bufs["tok"][:h], bufs["out"][:h],
+                                                  bufs["n"][:h], bufs["ws_g"])
+        return bound.bind_verify_greedy(g["target"][:h], bufs["tok"][:h], bufs["out"][:h], bufs["n"][:h],
+                                        bufs["ws_g"])
+
+    def sample():
+        if fused:
+            return bound.bind_verify_sample_fused(g["h_target"][h * T:], g["W"], bufs["tok"][h:], 1.0, 7,
+                                                  g["request_id"][h:], g["pos0"][h:], bufs["out"][h:],
+                                                  bufs["n"][h:], bufs["ws_v"])
+        return bound.bind_verify_sample(g["target"][h:], bufs["tok"][h:], 1.0, 7, g["request_id"][h:],
+                                        g["pos0"][h:], bufs["out"][h:], bufs["n"][h:], bufs["ws_v"])
+
     for c in calls:
         c()
+    if side is None:
+        greedy()()
+        sample()()
+    else:
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            greedy()()  # bound to, and enqueued on, the side stream
+        sample()()
+        main.wait_stream(side)
 
 
 def _snapshot(bufs):
@@ -59,10 +79,11 @@ def _same(a, b):
     return True
 
 
+@pytest.mark.parametrize("two_streams", [False, True])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name, overrides", [("c1_tiny", {"B": 4, "name": "c1_graph_b4"}),
                                               ("c1_tiny", {"B": 8, "D": 1024, "V": 20000, "name": "c1_graph_b8"})])
-def test_graph_replays_equal_eager(dfl, dev, name, overrides, fused):
+def test_graph_replays_equal_eager(dfl, dev, name, overrides, fused, two_streams):
     cfg = get_config(name, **overrides)
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in make_cycle_inputs(cfg).items()}
     B, T, P, M = cfg.B, cfg.T, cfg.P, cfg.M
@@ -87,9 +108,10 @@ def test_graph_replays_equal_eager(dfl, dev, name, overrides, fused):
     torch.cuda.synchronize()
     eager = _snapshot(bufs)
 
+    side = torch.cuda.Stream() if two_streams else None  # default priority
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        _cycle(dfl, g, cfg, bufs, dfl, fused)
+        _cycle(dfl, g, cfg, bufs, dfl, fused, side)
     for rep in range(3):
         for v in bufs.values():  # scribble over the outputs between replays
             for t in (v if isinstance(v, list) else [v]):
