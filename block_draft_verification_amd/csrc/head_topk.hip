@@ -597,20 +597,14 @@ __global__ __launch_bounds__(64 * WAVES) void head_skinny2_kernel(const uint16_t
 // from LDS and the accumulators stay in registers.  A strip as wide as the
 // M-block makes re-reading h from L2 cost no more than streaming W.  The
 // top-16 epilogue's candidate buffers reuse the chunk tile's LDS.
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
 struct WideCfg {
     static constexpr int THREADS = 128 * WN;          // 2 x WN wavefronts
     static constexpr int KC = 32 * KS;
     static constexpr int MB = 32 * MW;                // rows of h per workgroup
     static constexpr int NB = 16 * WN * NT;           // W rows per strip
-    // SWZ: unpadded rows whose 16-byte pieces are permuted (piece ^ (row & 6)),
-    // which keeps fragment reads free of bank conflicts (see piece_off) in
-    // 20 % less LDS than the padded pitch
-    static constexpr int ROWB = KC * 2 + (SWZ ? 0 : kPitchPad);
+    static constexpr int ROWB = KC * 2 + kPitchPad;
     static constexpr int PIECES = KC / 8;             // 16-byte pieces per row and chunk
-    static_assert(!SWZ || PIECES == 8, "the swizzle is laid out for 8 pieces per row");
-    // byte offset of piece pc of tile row `row` inside the row
-    static __device__ __forceinline__ int piece_off(int row, int pc) { return (SWZ ? (pc ^ (row & 6)) : pc) * 16; }
     static constexpr int RPL = THREADS / PIECES;      // rows per workgroup-wide load
     static constexpr int HLOADS = (MB + RPL - 1) / RPL;
     static constexpr int WLOADS = NB / RPL;
@@ -633,12 +627,12 @@ __device__ __forceinline__ void with_slot(int k, F&& f) {
     }
 }
 
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false, bool STATS = false>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool STATS = false>
 __global__ __launch_bounds__(128 * WN) __attribute__((amdgpu_waves_per_eu(WN / 2, WN / 2)))
 void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t M, int D,
                       int64_t V, int64_t n_tiles, int S, int n_mb, float* __restrict__ part_val,
                       int* __restrict__ part_idx, TileStats st) {
-    using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
+    using C = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
     constexpr int KC = C::KC;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char* lp = smem + C::LDS_BUF;
@@ -720,23 +714,21 @@ void head_wide_kernel(const uint16_t* __restrict__ h, const uint16_t* __restrict
             for (int q = 0; q < C::HLOADS; ++q) {
                 const int row = q * C::RPL + ri;
                 if (C::MB % C::RPL == 0 || row < C::MB)
-                    *reinterpret_cast<u32x4*>(tb + row * C::ROWB + C::piece_off(row, pj)) = hq[j][q];
+                    *reinterpret_cast<u32x4*>(tb + row * C::ROWB + pj * 16) = hq[j][q];
             }
             unsigned char* wb = tb + C::MB * C::ROWB;
 #pragma unroll
             for (int q = 0; q < C::WLOADS; ++q)
-                *reinterpret_cast<u32x4*>(wb + (q * C::RPL + ri) * C::ROWB + C::piece_off(q * C::RPL + ri, pj)) =
-                    wq[j][q];
+                *reinterpret_cast<u32x4*>(wb + (q * C::RPL + ri) * C::ROWB + pj * 16) = wq[j][q];
         };
         auto mfma_chunk = [&](int c, auto FULL) __attribute__((always_inline)) {
             constexpr bool full = decltype(FULL)::value;
             const unsigned char* tb = smem + (DBUF ? (size_t)(c & 1) * C::TILE : 0);
-            // fragment rows start at multiples of 16, so (row & 6) == (ln & 6)
             const unsigned char* ha = tb + (wm * 16 * MW + ln) * C::ROWB;
             const unsigned char* wbp = tb + (C::MB + wn * 16 + ln) * C::ROWB;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
-                const int po = C::piece_off(ln, 4 * s + lg);
+                const int po = (4 * s + lg) * 16;
                 // all of the k-step's fragments first, then its MFMAs
                 u32x4 b[NT], a[MW];
 #pragma unroll
@@ -1268,10 +1260,58 @@ __device__ __forceinline__ void strip_topk(const floatx4 (&acc)[MT][NT], const S
     }
 }
 
+// The softmax statistics of one strip's logits, still in the accumulators
+// (the target head of the fused sampler): per (row, 16-column vocabulary
+// tile) the tile maximum m and the float32 sum of exp2((z - m) * k2), as
+// stats_epilogue computes them, here from head_mfma_kernel's layout
+// (acc[i][t][q]: row 16 i + 4 (lane / 16) + q of the block, tile wave + 4 t
+// of the strip, column lane % 16 of the tile).
+template <int MT, int NT>
+__device__ __forceinline__ void mfma_stats_strip(const floatx4 (&acc)[MT][NT], const TileStats& st, int64_t m0,
+                                                 int rows_blk, int64_t col0, int wave, int lane_in, int nt_act,
+                                                 int64_t V) {
+    int lane = lane_in;
+    asm volatile("" : "+v"(lane));
+    const int ln = lane & 15, lg = lane >> 4;
+    auto rd = [](const float& x) __attribute__((always_inline)) {
+        float v;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+        return v;
+    };
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        if (t >= nt_act) continue;  // the wavefront's tiles past the strip's end
+        const int64_t tc = col0 + 16 * (wave + 4 * t);  // the tile's first column (< V)
+        const bool cok = tc + ln < V;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float z = rd(acc[i][t][q]);
+                float m = cok ? z : -INFINITY;
+                m = fmaxf(m, dpp_f32(m, ln, 1));
+                m = fmaxf(m, dpp_f32(m, ln, 2));
+                m = fmaxf(m, dpp_f32(m, ln, 4));
+                m = fmaxf(m, dpp_f32(m, ln, 8));
+                float e = cok ? __builtin_amdgcn_exp2f((z - m) * st.k2) : 0.0f;
+                e += dpp_f32(e, ln, 1);
+                e += dpp_f32(e, ln, 2);
+                e += dpp_f32(e, ln, 4);
+                e += dpp_f32(e, ln, 8);
+                const int r = 16 * i + 4 * lg + q;
+                if (ln == 0 && r < rows_blk) st.rec[(m0 + r) * st.n16 + tc / 16] = make_float2(m, e);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one fragment row at a time
+        }
+    }
+}
+
+// st.rec == nullptr: the top-16 lists into part_val / part_idx; otherwise the
+// softmax statistics of every (row, tile) into st.rec (part_* unused).
 template <int MT, int NT, int WAUX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, int64_t n_tiles, int S,
-                      int n_mb, float* __restrict__ part_val, int* __restrict__ part_idx) {
+                      int n_mb, float* __restrict__ part_val, int* __restrict__ part_idx, TileStats st) {
     // (h and W are deliberately not __restrict__: loads from restrict read-only
     // memory may be moved across the barrier asm, which would break the issue
     // order that the vmcnt waits count on)
@@ -1330,9 +1370,14 @@ void head_mfma_kernel(const uint16_t* h, const uint16_t* W, int64_t M, int D, in
             mfma_strip<MT, NT, NT / 2, WAUX>(hsrc, wsrc, D, nK, wave, lane, acc);
         else
             mfma_strip<MT, NT, 1, WAUX>(hsrc, wsrc, D, nK, wave, lane, acc);
-        strip_topk<MT, NT>(acc, sl, wave, lane, rows_blk, col0, nt_act, V, t0 == t_begin);
-        __syncthreads();  // the ring (epilogue scratch) is refilled by the next strip
+        if (st.rec) {
+            mfma_stats_strip<MT, NT>(acc, st, m0, rows_blk, col0, wave, lane, nt_act, V);
+        } else {
+            strip_topk<MT, NT>(acc, sl, wave, lane, rows_blk, col0, nt_act, V, t0 == t_begin);
+            __syncthreads();  // the ring (epilogue scratch) is refilled by the next strip
+        }
     }
+    if (st.rec) return;
     for (int e = tid; e < rows_blk * kTopK; e += 256) {
         const int r = e / kTopK, k = e % kTopK;
         const int64_t o = ((m0 + r) * S + slot) * kTopK + k;
@@ -1632,8 +1677,7 @@ __global__ __launch_bounds__(64 * kRankRows) void head_rank_kernel(int64_t M, in
 // ------------------------------------------------------------------ host
 namespace {
 
-enum HeadVariant { kSkinny = 0, kWide128 = 1, kWide224 = 2, kWide128W = 3, kWide64 = 4, kMfma128 = 5, kMfma224 = 6,
-                   kMfma240 = 7 };
+enum HeadVariant { kSkinny = 0, kWide64 = 1, kMfma128 = 2, kMfma224 = 3, kMfma240 = 4 };
 
 struct HeadPlan {
     HeadVariant variant;
@@ -1645,12 +1689,12 @@ struct HeadPlan {
 };
 
 // One instantiation of head_wide_kernel with its launch.
-template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN, bool SWZ = false>
+template <int MW, int NT, int KS, int DEPTH, bool DBUF, int WN>
 struct WideVariant {
-    using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN, SWZ>;
+    using Cfg = WideCfg<MW, NT, KS, DEPTH, DBUF, WN>;
     template <bool STATS>
     static const void* fn() {
-        return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ, STATS>);
+        return reinterpret_cast<const void*>(&head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, STATS>);
     }
     static void set_attr() {
         (void)hipFuncSetAttribute(fn<false>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
@@ -1660,7 +1704,7 @@ struct WideVariant {
     static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
                        int64_t n_tiles, float* pv, int* pi, hipStream_t stream, TileStats st = TileStats{}) {
         const int grid = (S + 7) / 8 * 8 * n_mb;
-        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, SWZ, STATS>), dim3(grid), dim3(Cfg::THREADS),
+        hipLaunchKernelGGL((head_wide_kernel<MW, NT, KS, DEPTH, DBUF, WN, STATS>), dim3(grid), dim3(Cfg::THREADS),
                            Cfg::LDS, stream, h, W, M, D, V, n_tiles, S, n_mb, pv, pi, st);
     }
 };
@@ -1679,15 +1723,16 @@ struct MfmaVariant {
         (void)hipFuncSetAttribute(fn<0>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
         (void)hipFuncSetAttribute(fn<kBufNT>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::LDS);
     }
+    // st.rec set: the statistics epilogue instead of the top-16 lists
     static void launch(int S, int n_mb, const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V,
-                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream) {
+                       int64_t n_tiles, float* pv, int* pi, hipStream_t stream, TileStats st = TileStats{}) {
         const int grid = (S + 7) / 8 * 8 * n_mb;
         if (n_mb == 1)
             hipLaunchKernelGGL((head_mfma_kernel<MT, NT, kBufNT>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M,
-                               D, V, n_tiles, S, n_mb, pv, pi);
+                               D, V, n_tiles, S, n_mb, pv, pi, st);
         else
             hipLaunchKernelGGL((head_mfma_kernel<MT, NT, 0>), dim3(grid), dim3(256), Cfg::LDS, stream, h, W, M, D, V,
-                               n_tiles, S, n_mb, pv, pi);
+                               n_tiles, S, n_mb, pv, pi, st);
     }
 };
 using Mfma128 = MfmaVariant<8, 4>;   // M-blocks of 128 rows, 256-row strips
@@ -1697,24 +1742,16 @@ using Mfma240 = MfmaVariant<15, 4>;  // M-blocks of 240 rows, 256-row strips
 // two workgroups of four wavefronts per CU (measured faster than one of eight)
 constexpr int kSkinnyNT = 2, kSkinnyKS = 4, kSkinnyWaves = 4, kSkinnyWG = 512;
 using SkinnyL = SkinnyLds<kSkinnyNT, kSkinnyKS, kSkinnyWaves>;
-// Measured on MI355X (V = 151936, D = 5120) among the register-feasible
-// instantiations: 8 wavefronts with 64x32 / 112x32 wavefront tiles (e.g. at
-// M = 224: 580-600 us for 224-row blocks, 795 us for two 128-row blocks; at
-// M = 480: 1400 us for four 128-row blocks, 1680 us for three 224-row ones).
-using Wide128 = WideVariant<4, 2, 2, 4, true, 4>;  // M-blocks of 128 rows
-using Wide224 = WideVariant<7, 2, 2, 2, true, 4>;  // M-blocks of 224 rows
-// several 128-row M-blocks (MFMA-bound sizes): 256-row strips in unpadded,
-// swizzled tiles, half the fragment reads per MFMA (M = 480: 1383 -> 1225 us)
-using Wide128W = WideVariant<4, 4, 2, 2, true, 4, true>;
 // at most 64 rows: 64-row blocks keep both wavefront rows busy (M = 56:
 // 306 us against 321 us with a 128-row block, whose second wavefront row
 // holds no rows; 256-row strips and deeper prefetch measured slower)
 using Wide64 = WideVariant<2, 2, 2, 4, true, 4>;
 constexpr int kCUs = 256;
 
-// stats: the plan of the softmax-statistics GEMMs (fused sampling), which
-// run on the LDS-staged wide kernels
-HeadPlan head_plan(int64_t M, int64_t V, bool stats = false) {
+// The same plan serves the top-16 head and the softmax-statistics GEMM of
+// the fused sampler (the skinny and 64-row kernels take a template flag for
+// the epilogue, head_mfma_kernel a run-time one).
+HeadPlan head_plan(int64_t M, int64_t V) {
     HeadPlan p{};
     p.n_tiles = (V + 15) / 16;
     // merge workgroups per row: spread the re-scoring of few rows over more CUs
@@ -1727,19 +1764,7 @@ HeadPlan head_plan(int64_t M, int64_t V, bool stats = false) {
         p.S = (int)std::min<int64_t>(kSkinnyWG, want);
         return p;
     }
-    if (stats && M > 64) {
-        const int64_t pad128 = (M + 127) / 128 * 128, pad224 = (M + 223) / 224 * 224;
-        if (M > 128 && pad224 <= pad128) {
-            p.variant = kWide224;
-            p.mb_rows = Wide224::Cfg::MB;
-        } else if (M > 128) {
-            p.variant = kWide128W;
-            p.mb_rows = Wide128W::Cfg::MB;
-        } else {
-            p.variant = kWide128;
-            p.mb_rows = Wide128::Cfg::MB;
-        }
-    } else if (M <= 64) {
+    if (M <= 64) {
         p.variant = kWide64;
         p.mb_rows = Wide64::Cfg::MB;
     } else {
@@ -1787,9 +1812,6 @@ static void set_head_attrs() {
         (void)hipFuncSetAttribute(
             reinterpret_cast<const void*>(&head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, true>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)SkinnyL::BYTES);
-        Wide128::set_attr();
-        Wide224::set_attr();
-        Wide128W::set_attr();
         Wide64::set_attr();
         Mfma128::set_attr();
         Mfma224::set_attr();
@@ -1813,14 +1835,8 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
                                dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M,
                                D, V, pv, pi, TileStats{});
             break;
-        case kWide128:
-            Wide128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
-            break;
         case kWide64:
             Wide64::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
-            break;
-        case kWide128W:
-            Wide128W::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
         case kMfma128:
             Mfma128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
@@ -1828,11 +1844,8 @@ int launch_head_topk(const uint16_t* h, const uint16_t* W, int64_t M, int D, int
         case kMfma224:
             Mfma224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
-        case kMfma240:
-            Mfma240::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
-            break;
         default:
-            Wide224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
+            Mfma240::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, pv, pi, stream);
             break;
     }
     int st = launch_status();
@@ -1901,24 +1914,24 @@ size_t head_stats_bytes(int64_t M, int64_t V) { return (size_t)M * ((V + 15) / 1
 int launch_head_stats(const uint16_t* h, const uint16_t* W, int64_t M, int D, int64_t V, double inv_tau,
                       float2* rec, hipStream_t stream) {
     set_head_attrs();
-    const HeadPlan p = head_plan(M, V, true);
+    const HeadPlan p = head_plan(M, V);
     const TileStats st{rec, (V + 15) / 16, (float)(inv_tau * 1.4426950408889634)};
     switch (p.variant) {
         case kSkinny:
             hipLaunchKernelGGL((head_skinny2_kernel<kSkinnyNT, kSkinnyKS, kSkinnyWaves, true>), dim3(p.S),
                                dim3(64 * kSkinnyWaves), SkinnyL::BYTES, stream, h, W, M, D, V, nullptr, nullptr, st);
             break;
-        case kWide128:
-            Wide128::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
-            break;
         case kWide64:
             Wide64::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
             break;
-        case kWide128W:
-            Wide128W::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+        case kMfma128:
+            Mfma128::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            break;
+        case kMfma224:
+            Mfma224::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
             break;
         default:
-            Wide224::launch<true>(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
+            Mfma240::launch(p.S, p.n_mb, h, W, M, D, V, p.n_tiles, nullptr, nullptr, stream, st);
             break;
     }
     return launch_status();

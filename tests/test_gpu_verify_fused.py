@@ -50,7 +50,10 @@ def test_matches_oracle(dfl, dev, B, T, D, V, grid):
 
 @pytest.mark.parametrize("B,T,D,V,tau,boost", [(8, 8, 256, 4096, 1.0, 6.0), (8, 8, 5120, 151936, 1.0, 8.0),
                                                (3, 16, 512, 3001, 0.7, 5.0), (8, 8, 5120, 151936, 1.0, 0.0),
-                                               (16, 8, 1024, 20000, 1.3, 7.0)])
+                                               (16, 8, 1024, 20000, 1.3, 7.0),
+                                               # the MFMA statistics GEMM: one 128-row block at the full
+                                               # vocabulary, and two 240-row blocks (M = 480)
+                                               (16, 8, 5120, 151936, 1.0, 8.0), (30, 16, 512, 9000, 1.0, 6.0)])
 def test_sample_fused_matches_oracle(dfl, dev, B, T, D, V, tau, boost):
     """Exact agreement with the sampler on exact logits, except for requests
     whose decisions lie within the float32 error of a boundary (margin 1e-5),
