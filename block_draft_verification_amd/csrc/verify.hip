@@ -17,6 +17,7 @@
 // decisions agree with an exact evaluation except within ~1e-15 of a boundary.
 
 #include "common.hpp"
+#include "exp64.hpp"
 #include "keysort.hpp"
 #include "philox.hpp"
 
@@ -277,12 +278,12 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_stats_kernel(
     for (int i = 1; i < kPerThread; ++i) m = fmaxf(m, v[i]);
     m = block_max(m, smax);
     const double md = (double)m;
-    // branch-free: an entry past the row end weighs exp(-inf) = 0, so all 16
+    // branch-free: an entry past the row end holds -inf and weighs exp64(-inf)
+    // = 0 (so does -inf - -inf, NaN, in a chunk of -inf logits), so all 16
     // exponentials are scheduled together and share their constants
     double s = 0.0;
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i)
-        s += exp(idx[i] != 0x7FFFFFFF ? ((double)v[i] - md) * inv_tau : -INFINITY);
+    for (int i = 0; i < kPerThread; ++i) s += exp64(((double)v[i] - md) * inv_tau);
     s = block_sum(s, ssum);
     if (threadIdx.x == 0) {
         ChunkStat cs;
@@ -333,7 +334,7 @@ __device__ int inverse_cdf_from(const float* __restrict__ row, int64_t V, int n_
             const int64_t e = e0 + j;
             double x = 0.0;
             if (e < V) {
-                x = exp(((double)row[e] - m) * inv_tau);
+                x = exp64(((double)row[e] - m) * inv_tau);
                 if ((mask >> j) & 1u) x = res.weight(e, x);
             }
             w[j] = x;
@@ -363,7 +364,7 @@ __device__ int last_positive(const float* __restrict__ row, int64_t V, double m,
         int best = -1;
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t e = c0 + (int64_t)threadIdx.x * kPerThread + j;
-            if (e < V && res.weight(e, exp(((double)row[e] - m) * inv_tau)) > 0.0) best = (int)e;
+            if (e < V && res.weight(e, exp64(((double)row[e] - m) * inv_tau)) > 0.0) best = (int)e;
         }
         best = -block_min_int(-best, iscr);
         if (best >= 0) return best;
@@ -414,7 +415,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
         const double m = (double)mf;
         double zpart = 0.0;
         for (int c = threadIdx.x; c < n_chunks; c += kVerifyThreads)
-            zpart += st[c].mass * exp(((double)st[c].m - m) * inv_tau);
+            zpart += st[c].mass * exp64(((double)st[c].m - m) * inv_tau);
         const double Z = block_sum(zpart, dscr);
         if (threadIdx.x == 0) {
             const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
@@ -426,7 +427,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
         if (s <= P) {
             const int d = draft[(int64_t)b * P + (s - 1)];
             const bool d_ok = d >= 0 && (int64_t)d < V;  // an id outside the vocabulary has p = 0
-            const double ed = d_ok ? exp(((double)row[d] - m) * inv_tau) : 0.0;
+            const double ed = d_ok ? exp64(((double)row[d] - m) * inv_tau) : 0.0;
             if (!QGEN) {
                 if (threadIdx.x == 0) {
                     res_id[0] = d_ok ? d : -1;
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
                             if (k2 < k) first = false;
                         }
                     }
-                    const double ev = first ? exp(((double)row[v] - m) * inv_tau) : 0.0;
+                    const double ev = first ? exp64(((double)row[v] - m) * inv_tau) : 0.0;
                     res_id[k] = first ? v : -1;
                     res_e[k] = ev;
                     res_w[k] = first ? fmax(0.0, ev - qsum * Z) : 0.0;
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_decide_kernel(
             const int c = c0 + threadIdx.x;
             double mass = 0.0;
             if (c < n_chunks) {
-                mass = st[c].mass * exp(((double)st[c].m - m) * inv_tau);
+                mass = st[c].mass * exp64(((double)st[c].m - m) * inv_tau);
                 for (int k = 0; k < n_res; ++k)
                     if (res_id[k] >= 0 && res_id[k] / kChunk == c) mass -= res_e[k] - res_w[k];
             }
@@ -577,7 +578,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
         const double m = (double)mf;
         double zp = 0.0;  // this run's mass
 #pragma unroll 8
-        for (int64_t i = i0; i < i1; ++i) zp += (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+        for (int64_t i = i0; i < i1; ++i) zp += (double)rr[i].y * exp64(((double)rr[i].x - m) * inv_tau);
         const double Z = block_sum(zp, dscr);
         if (tid == 0) {
             const Philox4 r = philox4x64_10(1ull, rid, (uint64_t)(p0 + s), 0ull, seed, 0ull);
@@ -590,7 +591,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
         if (s <= P) {
             const int d = draft[(int64_t)b * P + (s - 1)];
             const bool d_ok = d >= 0 && (int64_t)d < V;
-            if (d_ok) ed = exp((exact_logit(hr, W + (int64_t)d * D, D, dscr) - m) * inv_tau);
+            if (d_ok) ed = exp64((exact_logit(hr, W + (int64_t)d * D, D, dscr) - m) * inv_tau);
             if (s_u[0] * Z < ed) {
                 if (tid == 0) o[n] = d;
                 ++n;
@@ -606,7 +607,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
         // without the draft): each thread sums a contiguous run of tiles, one
         // block scan finds the run holding the target, its thread walks it
         auto tile_mass = [&](int64_t i) -> double {
-            double mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+            double mass = (double)rr[i].y * exp64(((double)rr[i].x - m) * inv_tau);
             if (skip >= 0 && skip / 16 == i) mass = fmax(0.0, mass - ed);
             return mass;
         };
@@ -614,7 +615,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
         double run = zp;
         if (skip >= 0 && skip / 16 >= i0 && skip / 16 < i1) {
             const int64_t i = skip / 16;
-            const double mass = (double)rr[i].y * exp(((double)rr[i].x - m) * inv_tau);
+            const double mass = (double)rr[i].y * exp64(((double)rr[i].x - m) * inv_tau);
             run -= mass - fmax(0.0, mass - ed);
         }
         double total;
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(kVerifyThreads) void sample_hidden_decide_kernel(
             for (int k = 0; k < 16; ++k) {
                 const int64_t v = hit * 16 + k;
                 if (v >= V || (int)v == skip) continue;
-                const double wv = exp((s_z[k] - m) * inv_tau);
+                const double wv = exp64((s_z[k] - m) * inv_tau);
                 if (wv > 0.0) last = (int)v;
                 c += wv;
                 if (tok < 0 && wv > 0.0 && c > target) tok = (int)v;
@@ -935,7 +936,7 @@ __global__ __launch_bounds__(kVerifyThreads) void topkp_set_kernel(const uint64_
             const bool real = lane < top_k && best != 0;
             const double lv = real ? (double)key_value(best) : 0.0;
             const double l0 = (double)key_value(readlane_u64(best, 0));
-            s_e[lane] = real ? exp((lv - l0) * inv_tau) : 0.0;
+            s_e[lane] = real ? exp64((lv - l0) * inv_tau) : 0.0;
             s_id[lane] = real ? key_id(best) : 0x7FFFFFFF;
         }
         __syncthreads();
