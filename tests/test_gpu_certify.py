@@ -98,3 +98,37 @@ def test_full_size_certificate(dfl, dev):
     if rows:
         ov, oi, _ = oracle_topk(h.cpu(), W.cpu(), rows=rows)
         assert np.array_equal(ti.cpu().numpy()[rows], oi)
+
+
+def test_near_ties_clustered_in_one_list_are_exact_or_uncertified(dfl, dev):
+    """Each request's 24 largest logits are near-ties (exact values within
+    ~1e-6 of 20, below float32 resolution there) on 24 consecutive vocabulary
+    ids, so one workgroup's partial list holds them and keeps only 16, in
+    float32 order.  An exact top-16 entry dropped there is never re-scored;
+    the certificate must then leave the row uncertified.  Every row is either
+    equal to the oracle's exact top-16 or not certified."""
+    rng = np.random.default_rng(21)
+    M, D, V = 8, 512, 20000
+    h = np.asarray(bf16(rng.standard_normal((M, D)), "cpu").float().numpy(), np.float64)
+    W = rng.standard_normal((V, D)) * 0.02
+    for m in range(M):
+        base = h[m] * (20.0 / (h[m] @ h[m]))
+        # variants of one row: two entries whose h values nearly agree swapped
+        order = np.argsort(h[m])
+        c0 = 1000 + 2000 * m
+        for k in range(24):
+            w = base.copy()
+            if k:
+                i, j = order[100 + 7 * k], order[101 + 7 * k]
+                w[i], w[j] = base[j], base[i]
+            W[c0 + k] = w
+    hd, Wd = bf16(h, dev), bf16(W, dev)
+    tv, ti, cert = dfl.head_topk_certified(hd, Wd, dfl.head_weight_bound(Wd))
+    ov, oi, _ = oracle_topk(hd.cpu(), Wd.cpu())
+    ti, cert = ti.cpu().numpy(), cert.cpu().numpy()
+    z = hd.float().cpu().numpy().astype(np.float64) @ Wd.float().cpu().numpy().astype(np.float64).T
+    for m in range(M):
+        top = np.argsort(-z[m], kind="stable")[:24]
+        assert np.all((top >= 1000 + 2000 * m) & (top < 1024 + 2000 * m)), m  # the planted cluster leads
+        assert np.array_equal(ti[m], oi[m]) or cert[m] == 0, (m, ti[m], oi[m])
+    assert np.all(cert == 0)  # no bound separates 16 of 24 near-ties
