@@ -365,6 +365,7 @@ int dflash_verify_sample_fused(const uint16_t* h_t, const uint16_t* W,
  *   request_id u64 [B], pos0 i64 [B] (absolute position of slot 0)
  *   outputs as for dflash_verify_greedy.
  * Requires B >= 1, 2 <= T <= 16, 1 <= V < 2^31, temperature finite and > 0.
+ * Logits must be finite or -inf (weight 0); a NaN logit also weighs 0.
  */
 int dflash_verify_sample(const float* logits, const int32_t* draft, int32_t B,
                          int32_t T, int64_t V, float temperature, uint64_t seed,
