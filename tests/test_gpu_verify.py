@@ -51,7 +51,9 @@ def sample(dfl, dev, L, d, tau, seed, rid, pos):
 
 @pytest.mark.parametrize("B,T,V,scale,tau", [(64, 8, 1000, 3.0, 1.0), (32, 8, 4097, 4.0, 1.0),
                                              (16, 8, 151936, 8.0, 1.0), (40, 5, 300, 2.0, 0.7),
-                                             (8, 16, 5000, 6.0, 1.3), (20, 2, 3, 1.0, 1.0)])
+                                             (8, 16, 5000, 6.0, 1.3), (20, 2, 3, 1.0, 1.0),
+                                             # tau 0.02: weights down to exp(-1e3), subnormal and zero
+                                             (16, 8, 5000, 4.0, 0.02)])
 def test_sample_matches_oracle_per_counter(dfl, dev, B, T, V, scale, tau):
     rng = np.random.default_rng(B * 3 + V)
     L = (rng.standard_normal((B, T, V)) * scale).astype(np.float32)
@@ -186,3 +188,32 @@ def test_batch_composition_invariance(dfl, dev):
     og_, ng_ = dfl.verify_greedy(torch.from_numpy(L).to(dev), torch.from_numpy(d).to(dev))
     og2, _ = dfl.verify_greedy(torch.from_numpy(L[perm]).to(dev), torch.from_numpy(d[perm]).to(dev))
     assert np.array_equal(og2.cpu().numpy(), og_.cpu().numpy()[perm])
+
+
+def test_sample_masked_logits(dfl, dev):
+    """Masked vocabulary entries (-inf logits: weight 0) are never accepted or
+    drawn, and the decisions equal the oracle's on the same logits.  NaN
+    entries weigh 0 as well (the header's contract), so logits with NaN at
+    those places give the same outputs as with -inf there."""
+    rng = np.random.default_rng(77)
+    B, T, V = 24, 8, 20000
+    L = (rng.standard_normal((B, T, V)) * 4.0).astype(np.float32)
+    mask = rng.random((B, T, V)) < 0.3
+    mask[:, :, 0] = False                               # no row is masked whole
+    g = np.argmax(np.where(mask, -np.inf, L), -1)
+    d = g[:, :T - 1].astype(np.int32)                   # mostly acceptable drafts
+    d[::2, 1] = np.argmax(mask[::2, 1], -1)             # half the requests draft a masked token at slot 2
+    Linf = np.where(mask, np.float32(-np.inf), L).astype(np.float32)
+    Lnan = np.where(mask, np.float32(np.nan), L).astype(np.float32)
+    rid = np.arange(B) * 5 + 2
+    pos = np.full(B, 40)
+    o1, n1 = sample(dfl, dev, Linf, d, 1.0, 9, rid, pos)
+    o0, n0, margin = osamp(Linf, d, 1.0, 9, rid, pos, return_margins=True)
+    ok = (o1 == o0).all(1) & (n1 == n0)
+    assert np.all(ok | (margin < 1e-12)) and (~ok).sum() <= 1, (np.nonzero(~ok), margin[~ok])
+    for b in range(B):
+        for t in range(n1[b]):
+            assert not mask[b, t, o1[b, t]], (b, t)     # every emitted token has weight > 0
+    assert np.all(n1[::2] <= 2)                          # a masked draft is rejected
+    o2, n2 = sample(dfl, dev, Lnan, d, 1.0, 9, rid, pos)
+    assert np.array_equal(o2, o1) and np.array_equal(n2, n1)
